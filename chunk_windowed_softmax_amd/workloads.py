@@ -1,0 +1,102 @@
+"""Named workloads and their seeded synthetic inputs.
+
+This module holds geometry and random-number recipes only -- none of the attention
+arithmetic -- so that both the HIP path's tests/benchmarks and the CPU oracle can be fed
+the very same tensors.
+
+Geometry comes from the VDN-Minimax-H3 window-attention article (lqnn.cn), §一: a
+packed sequence of T latent frames x S spatial tokens followed by G global (text /
+audio) tokens; chunks of K frames; window radius in chunks.  The head count and
+head size of the H3-scale workload follow sglang PR #43164 (56 heads, 7 per GPU under
+8-way head parallelism, head size 128).  The dense degenerate case is the non-causal
+video-VAE ViT decoder of sglang PR #34949.
+
+Input recipe (all configs): ``g = torch.Generator('cpu').manual_seed(seed)``; q, k, v
+are drawn with ``torch.randn(L, H, d, generator=g)`` in that order (fp32), then cast
+to the workload dtype with round-to-nearest-even.  For the ragged workload, a further
+``torch.randperm(L, generator=g)[:round(0.01 * L)]`` picks rows whose q and k are
+multiplied by 8 (exact in bf16) to stretch the softmax range.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Tuple
+
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    S: int
+    G: int
+    K: int
+    radius: int
+    H: int
+    d: int
+    dtype: torch.dtype
+    scaled_row_frac: float = 0.0
+    description: str = ""
+
+    @property
+    def L(self) -> int:
+        return self.T * self.S + self.G
+
+    @property
+    def geometry(self) -> Tuple[int, int, int, int, int]:
+        return (self.T, self.S, self.G, self.K, self.radius)
+
+    def with_heads(self, H: int) -> "Workload":
+        return Workload(self.name + f"_H{H}", self.T, self.S, self.G, self.K, self.radius, H, self.d,
+                        self.dtype, self.scaled_row_frac, self.description)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    "tiny": Workload("tiny", T=6, S=16, G=8, K=2, radius=1, H=1, d=64, dtype=torch.float32,
+                     description="6 frames x 16 tokens, K=2, radius 1, 8 globals, fp32"),
+    "small": Workload("small", T=24, S=256, G=256, K=3, radius=1, H=8, d=128, dtype=torch.bfloat16,
+                      description="24 frames x 256 tokens, K=3, radius 1, 256 globals, bf16"),
+    "h3": Workload("h3", T=102, S=960, G=1024, K=3, radius=1, H=7, d=128, dtype=torch.bfloat16,
+                   description="H3-scale one-GPU share: 102 latent frames x 960 tokens, K=3, radius 1, "
+                               "1024 globals, 7 heads (56/8), bf16"),
+    "h3_full": Workload("h3_full", T=102, S=960, G=1024, K=3, radius=1, H=56, d=128, dtype=torch.bfloat16,
+                        description="H3 scale with all 56 heads, bf16"),
+    "ragged": Workload("ragged", T=50, S=432, G=77, K=4, radius=2, H=16, d=128, dtype=torch.bfloat16,
+                       scaled_row_frac=0.01,
+                       description="50 frames (last chunk partial) x 432 tokens, K=4, radius 2, 77 globals, "
+                                   "1% of rows with q,k scaled x8, bf16"),
+    "dense": Workload("dense", T=8, S=1024, G=0, K=1, radius=8, H=16, d=64, dtype=torch.bfloat16,
+                      description="degenerate dense ViT case: radius >= chunk count, no globals, bf16"),
+}
+
+
+def make_inputs(w: Workload, seed: int = 0, device: str = "cpu"):
+    """Seeded q, k, v of shape [L, H, d] in the workload dtype (see module docstring)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    shape = (w.L, w.H, w.d)
+    q = torch.randn(shape, generator=g)
+    k = torch.randn(shape, generator=g)
+    v = torch.randn(shape, generator=g)
+    if w.scaled_row_frac > 0:
+        n = int(round(w.scaled_row_frac * w.L))
+        idx = torch.randperm(w.L, generator=g)[:n]
+        q[idx] *= 8.0
+        k[idx] *= 8.0
+    q, k, v = (x.to(w.dtype) for x in (q, k, v))
+    if device != "cpu":
+        q, k, v = (x.to(device) for x in (q, k, v))
+    return q, k, v
+
+
+def make_custom_inputs(L: int, H: int, d: int, dtype: torch.dtype, seed: int = 0, device: str = "cpu"):
+    """Seeded q, k, v for an arbitrary geometry (same recipe, no scaled rows)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    q = torch.randn((L, H, d), generator=g)
+    k = torch.randn((L, H, d), generator=g)
+    v = torch.randn((L, H, d), generator=g)
+    q, k, v = (x.to(dtype) for x in (q, k, v))
+    if device != "cpu":
+        q, k, v = (x.to(device) for x in (q, k, v))
+    return q, k, v

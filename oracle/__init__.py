@@ -1,0 +1,20 @@
+"""fp64 CPU oracle for chunk-windowed softmax attention -- test infrastructure only.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s ``cpu_baseline`` leg may
+import this package.  It shares no code with the HIP path.
+"""
+
+from .window_attention import (  # noqa: F401
+    Geometry,
+    PlanGroup,
+    chunk_span_rows,
+    kept_pairs_per_head,
+    kept_set,
+    masked_dense_attention,
+    plan_groups,
+    plan_kv_indices,
+    window_attention_reference,
+    window_attention_rows,
+    window_bounds,
+    window_mask,
+)
