@@ -1,0 +1,162 @@
+#!/usr/bin/env python3
+"""Benchmark of the decomposed chunk-windowed softmax attention on one MI355X.
+
+Metric: kept-pair TFLOP/s (4*d FLOP per kept (query, key) pair, all heads) and ms per
+call at the H3-scale one-GPU share (T=102 latent frames x S=960 tokens, K=3, radius 1,
+G=1024 global tokens, 7 heads of d=128, bf16), plus the fraction of MI355X's dense bf16
+MFMA peak.  One "step" is one wa_forward call (both legs and the merge) over inputs
+already resident in HBM.
+
+Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+HBM_PEAK_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="h3", help="workload name (h3, h3_full, small, ragged, dense)")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
+    ap.add_argument("--cpu-heads", type=int, default=1, help="heads of the workload the CPU oracle runs")
+    return ap.parse_args()
+
+
+def _cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(w, q, k, v, heads: int) -> dict:
+    """Time the fp64 oracle (as it stands) on the first `heads` heads of the workload."""
+    import numpy as np  # noqa: F401
+
+    from oracle import Geometry, kept_pairs_per_head, window_attention_reference
+
+    geom = Geometry(*w.geometry)
+    qs, ks, vs = (x[:, :heads].contiguous() for x in (q, k, v))
+    t0 = time.perf_counter()
+    window_attention_reference(qs, ks, vs, geom)
+    dt = time.perf_counter() - t0
+    flop = kept_pairs_per_head(geom) * heads * 4 * w.d
+    return {
+        "value": round(flop / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": _cpu_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 numpy per-frame oracle on {heads} of {w.H} heads of the {w.name} workload "
+                  f"(all {w.L} rows), {dt:.1f} s wall",
+        "seconds": round(dt, 3),
+    }
+
+
+def main() -> int:
+    args = _parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              f"(the path shards by heads across GPUs, which is not built here).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import chunk_windowed_softmax_amd as wa
+    from chunk_windowed_softmax_amd.workloads import WORKLOADS, make_inputs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    wa.load_library()
+    w = WORKLOADS[args.workload]
+    q_cpu, k_cpu, v_cpu = make_inputs(w, seed=0)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in (q_cpu, k_cpu, v_cpu))
+    out = torch.empty_like(q)
+
+    t0 = time.perf_counter()
+    plan = wa.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info
+    flop = info["kept_pairs_per_head"] * w.H * 4 * w.d
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        wa.wa_forward(plan, q, k, v, out=out, stream=stream)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        wa.wa_forward(plan, q, k, v, out=out, stream=stream)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per_call = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ms_med = statistics.median(per_call)
+    ms_min = min(per_call)
+    ms_mean = statistics.fmean(per_call)
+    ms_step = wall * 1e3 / args.steps
+
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (ms_mean * 1e-3) / 1e12
+    res = {
+        "metric": "kept-pair TFLOP/s at the H3-scale window call on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "T": w.T, "S": w.S, "G": w.G, "K": w.K, "radius": w.radius,
+            "H": w.H, "d": w.d, "L": w.L, "kept_pairs": info["kept_pairs_per_head"] * w.H,
+            "flop_per_call": flop, "n_groups": info["n_groups"], "n_splits": info["n_splits"],
+            "parallelism": "single GPU",
+        },
+        "ms_per_call": {"median": round(ms_med, 4), "min": round(ms_min, 4), "mean": round(ms_mean, 4)},
+        "pct_of_bf16_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "plan_create_ms": round(plan_ms, 3),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_kernel (+ split merge) per wa_forward call, HIP events on the launch stream",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_heads)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,200 @@
+"""Chunk-windowed softmax attention for MI355X (gfx950): thin Python binding.
+
+The work happens in ``libwa.so`` (HIP kernels behind the C ABI of ``include/wa.h``);
+this module only marshals arguments.  PyTorch provides device memory and the current
+stream.  There is no fallback: if the library is missing the calls raise.
+
+Functions carry the C names:
+
+* ``wa_plan_create(T, S, G, K, radius, H, d) -> Plan``
+* ``wa_forward(plan, q, k, v, out=None) -> out``
+* ``wa_plan_info / wa_plan_groups / wa_plan_kv_indices / wa_plan_items / wa_last_error``
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libwa.so")
+
+WA_OK, WA_ERR_INVALID, WA_ERR_UNSUPPORTED, WA_ERR_ALLOC, WA_ERR_HIP = range(5)
+WA_BF16, WA_F32 = 0, 1
+WA_ITEM_COLS = 8
+
+# Every symbol include/wa.h declares.
+EXPORTED_SYMBOLS = (
+    "wa_plan_create",
+    "wa_plan_release",
+    "wa_forward",
+    "wa_plan_info",
+    "wa_plan_groups",
+    "wa_plan_kv_indices",
+    "wa_plan_items",
+    "wa_last_error",
+)
+
+
+class WaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[wa status {code}] {msg}")
+        self.code = code
+
+
+class _PlanInfo(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_int32), ("S", ctypes.c_int32), ("G", ctypes.c_int32), ("K", ctypes.c_int32),
+        ("radius", ctypes.c_int32), ("H", ctypes.c_int32), ("d", ctypes.c_int32), ("L", ctypes.c_int32),
+        ("n_chunks", ctypes.c_int32), ("n_groups", ctypes.c_int32), ("kept_pairs_per_head", ctypes.c_int64),
+        ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("n_splits", ctypes.c_int32),
+        ("n_items", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load ``libwa.so`` (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m chunk_windowed_softmax_amd.build`")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.wa_plan_create.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(P)]
+    lib.wa_plan_release.argtypes = [P]
+    lib.wa_forward.argtypes = [P, P, P, P, P, ctypes.c_int, P]
+    lib.wa_plan_info.argtypes = [P, ctypes.POINTER(_PlanInfo)]
+    lib.wa_plan_groups.argtypes = [P, i32p, ctypes.c_size_t]
+    lib.wa_plan_kv_indices.argtypes = [P, ctypes.c_int, i32p, ctypes.c_size_t]
+    lib.wa_plan_items.argtypes = [P, i32p, ctypes.c_size_t]
+    lib.wa_last_error.argtypes = []
+    lib.wa_last_error.restype = ctypes.c_char_p
+    for name in EXPORTED_SYMBOLS:
+        if name != "wa_last_error":
+            getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def wa_last_error() -> str:
+    return load_library().wa_last_error().decode()
+
+
+def _check(code: int) -> None:
+    if code != WA_OK:
+        raise WaError(code, wa_last_error())
+
+
+class Plan:
+    """Handle of a cached plan (one reference, released on garbage collection)."""
+
+    def __init__(self, handle: ctypes.c_void_p):
+        self._h = handle
+        self.info = wa_plan_info(self)
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._h
+
+    def release(self) -> None:
+        if self._h:
+            _check(load_library().wa_plan_release(self._h))
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+
+def wa_plan_create(T: int, S: int, G: int, K: int, radius: int, H: int, d: int) -> Plan:
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.wa_plan_create(T, S, G, K, radius, H, d, ctypes.byref(h)))
+    return Plan(h)
+
+
+def wa_plan_info(plan: Plan) -> dict:
+    info = _PlanInfo()
+    _check(load_library().wa_plan_info(plan.handle, ctypes.byref(info)))
+    return {name: getattr(info, name) for name, _ in _PlanInfo._fields_}
+
+
+def _int32_buffer(n: int):
+    arr = np.zeros(max(n, 1), dtype=np.int32)
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def wa_plan_groups(plan: Plan) -> np.ndarray:
+    n = plan.info["n_groups"] * 6
+    arr, ptr = _int32_buffer(n)
+    _check(load_library().wa_plan_groups(plan.handle, ptr, arr.size))
+    return arr[:n].reshape(-1, 6)
+
+
+def wa_plan_kv_indices(plan: Plan, g: int) -> np.ndarray:
+    groups = wa_plan_groups(plan)
+    if not 0 <= g < len(groups):
+        n = 1
+    else:
+        n = int(groups[g, 3] - groups[g, 2]) + plan.info["G"]
+    arr, ptr = _int32_buffer(n)
+    _check(load_library().wa_plan_kv_indices(plan.handle, g, ptr, arr.size))
+    return arr[:n]
+
+
+def wa_plan_items(plan: Plan) -> np.ndarray:
+    n = plan.info["n_items"] * WA_ITEM_COLS
+    arr, ptr = _int32_buffer(n)
+    _check(load_library().wa_plan_items(plan.handle, ptr, arr.size))
+    return arr[:n].reshape(-1, WA_ITEM_COLS)
+
+
+def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
+    """Run the decomposed window attention; returns ``out`` ([L, H, d], dtype of q).
+
+    q, k, v: contiguous CUDA (HIP) tensors [L, H, d] of one dtype, bfloat16 or float32.
+    ``stream``: a torch stream (default: the current stream).
+    """
+    import torch
+
+    info = plan.info
+    shape = (info["L"], info["H"], info["d"])
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported dtype {dtype}; use bfloat16 or float32")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {shape}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if out is None:
+        out = torch.empty(shape, dtype=dtype, device=q.device)
+    elif tuple(out.shape) != shape or out.dtype != dtype or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous GPU tensor with the shape and dtype of q")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    code = WA_F32 if dtype == torch.float32 else WA_BF16
+    with torch.cuda.device(q.device):
+        _check(load_library().wa_forward(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                         code, ctypes.c_void_p(stream.cuda_stream)))
+    return out
+
+
+__all__ = [
+    "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
+    "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
+]

@@ -1,0 +1,298 @@
+// C ABI of the chunk-windowed softmax attention library: plan cache, argument checks,
+// device resources and launches.  Declarations and contracts: include/wa.h.
+//
+// Plans are cached by geometry, at most four (lqnn.cn article on VDN-Minimax-H3 window
+// attention, §三: the decomposed form's plan is cached per geometry shape, four plans).
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <list>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+
+#include "../../include/wa.h"
+#include "launch.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+struct DeviceResources {
+  wa::Item* items = nullptr;
+  float* part = nullptr;     // partial O then partial (m, l) of the global leg
+  void* staging = nullptr;   // bf16 copies of fp32 q, k, v (allocated on first fp32 call)
+  int64_t staging_bytes = 0;
+};
+
+}  // namespace
+
+struct wa_plan {
+  wa::HostPlan host;
+  std::atomic<int> refs{1};
+  std::atomic<bool> cached{true};
+  std::mutex dev_mu;
+  std::map<int, DeviceResources> dev;
+
+  ~wa_plan() {
+    int prev = -1;
+    if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+    for (auto& kv : dev) {
+      if (hipSetDevice(kv.first) != hipSuccess) continue;
+      if (kv.second.items) (void)hipFree(kv.second.items);
+      if (kv.second.part) (void)hipFree(kv.second.part);
+      if (kv.second.staging) (void)hipFree(kv.second.staging);
+    }
+    if (prev >= 0) (void)hipSetDevice(prev);
+  }
+};
+
+namespace {
+
+constexpr size_t kCacheCapacity = 4;
+std::mutex g_cache_mu;
+std::list<wa_plan*> g_cache;  // front = most recently created or fetched
+
+void unref(wa_plan* p) {
+  if (p->refs.fetch_sub(1) == 1) delete p;
+}
+
+// Device tables and workspace of `p` on the current device (created on first use).
+int device_resources(wa_plan* p, DeviceResources** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(p->dev_mu);
+  auto found = p->dev.find(dev);
+  if (found != p->dev.end()) {
+    *out = &found->second;
+    return WA_OK;
+  }
+  DeviceResources r;
+  const size_t item_bytes = p->host.items.size() * sizeof(wa::Item);
+  e = hipMalloc(&r.items, item_bytes);
+  if (e != hipSuccess) return fail(WA_ERR_ALLOC, std::string("hipMalloc(items): ") + hipGetErrorString(e));
+  e = hipMemcpy(r.items, p->host.items.data(), item_bytes, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(r.items);
+    return fail(WA_ERR_HIP, std::string("hipMemcpy(items): ") + hipGetErrorString(e));
+  }
+  if (p->host.partial_bytes > 0) {
+    e = hipMalloc(&r.part, (size_t)p->host.partial_bytes);
+    if (e != hipSuccess) {
+      (void)hipFree(r.items);
+      return fail(WA_ERR_ALLOC, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
+    }
+  }
+  *out = &(p->dev[dev] = r);
+  return WA_OK;
+}
+
+bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) == 0; }
+
+bool overlaps(const void* a, const void* b, size_t n) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + n && y < x + n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan** out) {
+  if (!out) return fail(WA_ERR_INVALID, "wa_plan_create: out is NULL");
+  *out = nullptr;
+  const wa::Geometry geo{T, S, G, K, radius, H, d};
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
+      if ((*it)->host.geo == geo) {
+        wa_plan* p = *it;
+        g_cache.erase(it);
+        g_cache.push_front(p);
+        p->refs.fetch_add(1);
+        *out = p;
+        return WA_OK;
+      }
+    }
+  }
+  wa::HostPlan hp;
+  std::string err;
+  const int st = wa::build_plan(geo, &hp, &err);
+  if (st != 0) return fail(st, "wa_plan_create: " + err);
+  wa_plan* p = nullptr;
+  try {
+    p = new wa_plan();
+  } catch (...) {
+    return fail(WA_ERR_ALLOC, "wa_plan_create: out of host memory");
+  }
+  p->host = std::move(hp);
+  p->refs.store(2);  // the caller's handle + the cache's
+  wa_plan* evicted = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_cache_mu);
+    for (wa_plan* other : g_cache) {
+      if (other->host.geo == geo) {  // another thread built the same plan meanwhile
+        other->refs.fetch_add(1);
+        delete p;
+        *out = other;
+        return WA_OK;
+      }
+    }
+    g_cache.push_front(p);
+    if (g_cache.size() > kCacheCapacity) {
+      evicted = g_cache.back();
+      g_cache.pop_back();
+      evicted->cached.store(false);
+    }
+  }
+  if (evicted) unref(evicted);
+  *out = p;
+  return WA_OK;
+}
+
+int wa_plan_release(wa_plan* plan) {
+  if (!plan) return fail(WA_ERR_INVALID, "wa_plan_release: plan is NULL");
+  unref(plan);
+  return WA_OK;
+}
+
+int wa_plan_info(const wa_plan* plan, wa_plan_info_t* info) {
+  if (!plan || !info) return fail(WA_ERR_INVALID, "wa_plan_info: NULL argument");
+  const wa::HostPlan& h = plan->host;
+  std::memset(info, 0, sizeof(*info));
+  info->T = h.geo.T;
+  info->S = h.geo.S;
+  info->G = h.geo.G;
+  info->K = h.geo.K;
+  info->radius = h.geo.radius;
+  info->H = h.geo.H;
+  info->d = h.geo.d;
+  info->L = h.L;
+  info->n_chunks = h.n_chunks;
+  info->n_groups = (int32_t)h.groups.size();
+  info->kept_pairs_per_head = h.kept_pairs_per_head;
+  info->block_m = h.block_m;
+  info->block_n = h.block_n;
+  info->n_splits = h.n_splits;
+  info->n_items = (int32_t)h.items.size();
+  info->workspace_bytes = h.partial_bytes;
+  return WA_OK;
+}
+
+int wa_plan_groups(const wa_plan* plan, int32_t* dst, size_t n) {
+  if (!plan || !dst) return fail(WA_ERR_INVALID, "wa_plan_groups: NULL argument");
+  const auto& g = plan->host.groups;
+  if (n < g.size() * 6) return fail(WA_ERR_INVALID, "wa_plan_groups: destination too small");
+  for (size_t i = 0; i < g.size(); ++i) {
+    dst[6 * i + 0] = g[i].q_begin;
+    dst[6 * i + 1] = g[i].q_end;
+    dst[6 * i + 2] = g[i].kv_begin;
+    dst[6 * i + 3] = g[i].kv_end;
+    dst[6 * i + 4] = g[i].chunk_lo;
+    dst[6 * i + 5] = g[i].chunk_hi;
+  }
+  return WA_OK;
+}
+
+int wa_plan_kv_indices(const wa_plan* plan, int g, int32_t* dst, size_t n) {
+  if (!plan || !dst) return fail(WA_ERR_INVALID, "wa_plan_kv_indices: NULL argument");
+  const wa::HostPlan& h = plan->host;
+  if (g < 0 || g >= (int)h.groups.size()) return fail(WA_ERR_INVALID, "wa_plan_kv_indices: bad group index");
+  const wa::Group& gr = h.groups[g];
+  const size_t need = size_t(gr.kv_end - gr.kv_begin) + size_t(h.geo.G);
+  if (n < need) return fail(WA_ERR_INVALID, "wa_plan_kv_indices: destination too small");
+  size_t o = 0;
+  for (int32_t j = gr.kv_begin; j < gr.kv_end; ++j) dst[o++] = j;
+  for (int32_t j = h.n_frame_rows; j < h.L; ++j) dst[o++] = j;
+  return WA_OK;
+}
+
+int wa_plan_items(const wa_plan* plan, int32_t* dst, size_t n) {
+  if (!plan || !dst) return fail(WA_ERR_INVALID, "wa_plan_items: NULL argument");
+  const auto& items = plan->host.items;
+  if (n < items.size() * WA_ITEM_COLS) return fail(WA_ERR_INVALID, "wa_plan_items: destination too small");
+  std::memcpy(dst, items.data(), items.size() * sizeof(wa::Item));
+  return WA_OK;
+}
+
+int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v, void* out, int dtype,
+               void* stream_v) {
+  if (!cplan) return fail(WA_ERR_INVALID, "wa_forward: plan is NULL");
+  if (!q || !k || !v || !out) return fail(WA_ERR_INVALID, "wa_forward: NULL tensor pointer");
+  if (dtype != WA_BF16 && dtype != WA_F32) return fail(WA_ERR_INVALID, "wa_forward: dtype must be WA_BF16 or WA_F32");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(WA_ERR_INVALID, "wa_forward: tensors must be 16-byte aligned");
+  wa_plan* plan = const_cast<wa_plan*>(cplan);
+  const wa::HostPlan& h = plan->host;
+  const int64_t elems = int64_t(h.L) * h.geo.H * h.geo.d;
+  const size_t esize = dtype == WA_F32 ? 4 : 2;
+  const size_t bytes = size_t(elems) * esize;
+  if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+    return fail(WA_ERR_INVALID, "wa_forward: out overlaps an input");
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+
+  DeviceResources* r = nullptr;
+  int st = device_resources(plan, &r);
+  if (st != WA_OK) return st;
+
+  const void *qb = q, *kb = k, *vb = v;
+  if (dtype == WA_F32) {
+    const int64_t need = 3 * elems * 2;
+    {
+      std::lock_guard<std::mutex> lk(plan->dev_mu);
+      if (r->staging_bytes < need) {
+        if (r->staging) (void)hipFree(r->staging);
+        r->staging = nullptr;
+        r->staging_bytes = 0;
+        hipError_t e = hipMalloc(&r->staging, (size_t)need);
+        if (e != hipSuccess) return fail(WA_ERR_ALLOC, std::string("hipMalloc(staging): ") + hipGetErrorString(e));
+        r->staging_bytes = need;
+      }
+    }
+    char* s = static_cast<char*>(r->staging);
+    const void* src[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+      hipError_t e = wa::launch_f32_to_bf16(static_cast<const float*>(src[i]), s + i * elems * 2, elems, stream);
+      if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("f32_to_bf16 launch: ") + hipGetErrorString(e));
+    }
+    qb = s;
+    kb = s + elems * 2;
+    vb = s + 2 * elems * 2;
+  }
+
+  wa::ForwardArgs a;
+  a.q = qb;
+  a.k = kb;
+  a.v = vb;
+  a.out = out;
+  a.out_f32 = dtype == WA_F32;
+  a.d = h.geo.d;
+  a.H = h.geo.H;
+  a.L = h.L;
+  a.G = h.geo.G;
+  a.frame_rows = h.n_frame_rows;
+  a.items = r->items;
+  a.n_items = (int)h.items.size();
+  a.n_splits = h.n_splits;
+  a.part_o = r->part;
+  a.part_ml = r->part ? r->part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;
+  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(h.geo.d)));
+  hipError_t e = wa::launch_forward(a, stream);
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward launch: ") + hipGetErrorString(e));
+  return WA_OK;
+}
+
+const char* wa_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

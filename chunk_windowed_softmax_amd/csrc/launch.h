@@ -1,0 +1,34 @@
+// Internal interface between the C ABI and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "plan.h"
+
+namespace wa {
+
+struct ForwardArgs {
+  const void* q;          // bf16 [L, H, d]
+  const void* k;          // bf16 [L, H, d]
+  const void* v;          // bf16 [L, H, d]
+  void* out;              // [L, H, d], bf16 or fp32 (out_f32)
+  bool out_f32;
+  int d, H, L, G, frame_rows;
+  const Item* items;      // device copy of the plan's items
+  int n_items;
+  int n_splits;           // > 1: global-leg items write partials, then a combine pass
+  float* part_o;          // [n_splits, G, H, d] fp32
+  float* part_ml;         // [n_splits, G, H, 2] fp32: running max (log2 units), row sum
+  float scale_log2;       // log2(e) / sqrt(d)
+};
+
+// Enqueue the attention pass (both legs) and, when the global leg is split, the combine
+// pass on `stream`.
+hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
+
+// Enqueue an fp32 -> bf16 (round to nearest even) conversion of n elements (n % 4 == 0).
+hipError_t launch_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_t stream);
+
+}  // namespace wa

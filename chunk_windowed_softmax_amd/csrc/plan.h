@@ -1,0 +1,59 @@
+// Host-side plan of the decomposed chunk-windowed attention (no HIP dependency).
+//
+// The decomposition follows the lqnn.cn article on VDN-Minimax-H3 window attention:
+// §一 gives the window rule (chunks of K latent frames, whole chunks within +-radius of
+// the frame's chunk, global tokens fully connected); §三 groups query rows with identical
+// kept-KV sets into plain dense attentions, runs the window groups and the global rows as
+// two legs with disjoint row sets, and caches the plan by geometry.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace wa {
+
+struct Geometry {
+  int T, S, G, K, radius, H, d;
+  bool operator==(const Geometry& o) const {
+    return T == o.T && S == o.S && G == o.G && K == o.K && radius == o.radius && H == o.H && d == o.d;
+  }
+};
+
+struct Group {  // a maximal run of chunks sharing one window
+  int32_t q_begin, q_end, kv_begin, kv_end, chunk_lo, chunk_hi;
+};
+
+struct Item {  // one block_m-row query tile over up to two key segments (all heads alike)
+  int32_t q_begin, q_end;
+  int32_t kv0_begin, kv0_end;
+  int32_t kv1_begin, kv1_end;
+  int32_t split;     // -1: final rows; s >= 0: partial result of key split s (global leg)
+  int32_t reserved;
+};
+static_assert(sizeof(Item) == 32, "Item is uploaded as 8 int32");
+
+struct HostPlan {
+  Geometry geo{};
+  int32_t L = 0, n_frame_rows = 0, n_chunks = 0;
+  int64_t kept_pairs_per_head = 0;
+  int32_t block_m = 0, block_n = 0, n_splits = 0;
+  int32_t n_window_items = 0;
+  std::vector<Group> groups;
+  std::vector<Item> items;  // window items (group-major), then global-leg items (split-major)
+  int64_t partial_bytes = 0;  // device workspace of the global leg's partial results
+};
+
+constexpr int kBlockM = 128;  // 4 waves x 32 query rows
+constexpr int kBlockN = 64;   // keys per staged K/V tile
+
+// Status codes mirror the C ABI (0 ok, 1 invalid, 2 unsupported).
+int build_plan(const Geometry& g, HostPlan* out, std::string* err);
+
+// Chunk window [lo, hi] of chunk c (clipped to existing chunks).
+inline void chunk_window(int c, int n_chunks, int radius, int* lo, int* hi) {
+  *lo = c - radius < 0 ? 0 : c - radius;
+  *hi = c + radius > n_chunks - 1 ? n_chunks - 1 : c + radius;
+}
+
+}  // namespace wa

@@ -1,0 +1,158 @@
+/*
+ * wa.h -- C ABI of the chunk-windowed softmax attention library (gfx950 / MI355X).
+ *
+ * What it computes.  The softmax window branch of VDN-H3's HybridAttention, as
+ * described in the lqnn.cn article on VDN-Minimax-H3 window attention:
+ *   - §一: the input is one packed sequence of T latent frames x S spatial tokens,
+ *     followed by G global (text / audio) tokens.  Every K latent frames form a chunk;
+ *     frame t (chunk c = t / K) attends to all tokens of the whole chunks whose index
+ *     lies in [c - radius, c + radius] (clipped to the chunks that exist) and to every
+ *     global token; global tokens attend to the whole sequence.
+ *   - §三: the "decomposed" form.  Query rows with an identical kept-KV set form one
+ *     group and each group is one plain mask-free dense attention; the window groups
+ *     and the global rows are two legs whose row sets are disjoint and together cover
+ *     the sequence, and their results are scattered into one contiguous output.  The
+ *     plan (groups, index construction) is cached by geometry, at most four plans.
+ * Softmax scale is 1/sqrt(d) (inputs are not pre-scaled).  Attention is non-causal.
+ *
+ * Layout.  q, k, v and out are dense row-major [L, H, d] tensors, L = T*S + G, rows in
+ * the packed order (frame-major frame rows t*S + s, then the G global rows), row
+ * stride H*d elements -- the [B, L, H, d] layout of the H3 attention modules in sglang
+ * PR #34949 with B = 1.  A caller with a batch calls once per sequence.
+ *
+ * Status codes.  Every function returns WA_OK (0) or one of the WA_ERR_* codes; no
+ * exception or abort crosses this boundary.  After a non-zero status, wa_last_error()
+ * returns a message for the calling thread.  Device faults inside a kernel surface at
+ * the caller's next synchronisation, not as a status of wa_forward.
+ */
+#ifndef WA_H_
+#define WA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  WA_OK = 0,
+  WA_ERR_INVALID = 1,     /* invalid argument (geometry, pointer, alignment, size) */
+  WA_ERR_UNSUPPORTED = 2, /* valid but not supported (head size, dtype, index range) */
+  WA_ERR_ALLOC = 3,       /* host or device allocation failed */
+  WA_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+};
+
+/* Element types of q, k, v and out (all four share one type). */
+enum {
+  WA_BF16 = 0, /* bfloat16: computed with bf16 MFMA products, fp32 softmax/accumulators */
+  WA_F32 = 1   /* float32 in and out: rounded to bf16 (nearest-even) for the products */
+};
+
+/* Opaque, reference-counted plan for one geometry. */
+typedef struct wa_plan wa_plan;
+
+/* Summary of a plan (filled by wa_plan_info). */
+typedef struct wa_plan_info_t {
+  int32_t T, S, G, K, radius, H, d; /* the geometry the plan was built for */
+  int32_t L;                        /* T*S + G rows */
+  int32_t n_chunks;                 /* ceil(T / K) */
+  int32_t n_groups;                 /* window groups (first leg) */
+  int64_t kept_pairs_per_head;      /* kept (query, key) pairs of one head */
+  int32_t block_m;                  /* query rows per work item */
+  int32_t block_n;                  /* keys per staged K/V tile */
+  int32_t n_splits;                 /* key splits of the global leg (1 = no split) */
+  int32_t n_items;                  /* work items per head (both legs) */
+  int64_t workspace_bytes;          /* device workspace of the global leg's partials */
+} wa_plan_info_t;
+
+/* Columns of one row of wa_plan_items(). */
+enum {
+  WA_ITEM_Q_BEGIN = 0, /* first query row of the item */
+  WA_ITEM_Q_END,       /* one past the last query row (at most block_m rows) */
+  WA_ITEM_KV0_BEGIN,   /* first key segment [begin, end) */
+  WA_ITEM_KV0_END,
+  WA_ITEM_KV1_BEGIN,   /* second key segment [begin, end); empty when begin == end */
+  WA_ITEM_KV1_END,
+  WA_ITEM_SPLIT,       /* -1: writes normalised output rows; s >= 0: split s of the global leg */
+  WA_ITEM_RESERVED,
+  WA_ITEM_COLS
+};
+
+/*
+ * wa_plan_create -- build (or fetch from the cache) the plan of one geometry.
+ *
+ * The plan holds the window groups of §三 (maximal runs of consecutive chunks whose
+ * windows are identical), each group's kept-KV list (its chunk span followed by the
+ * global rows), the global leg (rows [T*S, L) over keys [0, L), split into n_splits
+ * key ranges), and the work items the kernels run.  Plans are cached by the seven
+ * arguments; at most four are cached, least recently created-or-fetched evicted first.
+ *
+ * Arguments: T, S, K, H >= 1; G >= 0; radius >= 0; d in {64, 128}; L*H*d < 2^31.
+ * On success *out receives a handle that the caller owns one reference of; release it
+ * with wa_plan_release.  Building a plan touches no device: device tables and the
+ * workspace are created on the first wa_forward on each device.
+ * Errors: WA_ERR_INVALID (bad geometry or out == NULL), WA_ERR_UNSUPPORTED (d, index
+ * range), WA_ERR_ALLOC.
+ */
+int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan** out);
+
+/*
+ * wa_plan_release -- drop one reference.  The plan (and its device memory) is freed
+ * once no handle refers to it and the cache no longer holds it.  Releasing a handle more
+ * often than it was obtained is undefined.  WA_ERR_INVALID for NULL.
+ */
+int wa_plan_release(wa_plan* plan);
+
+/*
+ * wa_forward -- run the decomposed window attention of §三 for one packed sequence.
+ *
+ * q, k, v: device pointers to [L, H, d] tensors of element type `dtype` (WA_BF16 or
+ * WA_F32), 16-byte aligned, caller-owned, read only.  out: device pointer to an [L, H, d]
+ * tensor of the same type, 16-byte aligned, caller-owned, written in full (every row and
+ * head exactly once); it must not overlap q, k or v.  stream: a hipStream_t (NULL = the
+ * default stream); all work is enqueued on it and the call returns without
+ * synchronising.  The first call on a device allocates the plan's device tables and
+ * workspace (and, for WA_F32, a bf16 staging copy of q, k, v); later calls allocate
+ * nothing.  Concurrent calls with one plan on different streams race on the plan's
+ * workspace: serialise them.
+ * Errors: WA_ERR_INVALID (NULL / misaligned / overlapping pointers, bad dtype),
+ * WA_ERR_ALLOC, WA_ERR_HIP (launch failure).
+ */
+int wa_forward(const wa_plan* plan, const void* q, const void* k, const void* v, void* out,
+               int dtype, void* stream);
+
+/* wa_plan_info -- fill *info.  WA_ERR_INVALID for NULL arguments. */
+int wa_plan_info(const wa_plan* plan, wa_plan_info_t* info);
+
+/*
+ * wa_plan_groups -- copy the window groups to host memory: n_groups rows of six int32
+ * {q_begin, q_end, kv_begin, kv_end, chunk_lo, chunk_hi}; rows [q_begin, q_end) attend
+ * to keys [kv_begin, kv_end) (the span of chunks chunk_lo..chunk_hi) plus the global
+ * rows.  `n` is the capacity of dst in int32 elements; WA_ERR_INVALID if it is too small.
+ */
+int wa_plan_groups(const wa_plan* plan, int32_t* dst, size_t n);
+
+/*
+ * wa_plan_kv_indices -- copy group g's explicit ascending kept-KV index list (chunk
+ * span, then the global rows) to host memory: (kv_end - kv_begin + G) int32.  These are
+ * the gather indices of the decomposed form; the kernels never materialise them (they
+ * read the span and the global rows in place).  WA_ERR_INVALID for a bad g or small n.
+ */
+int wa_plan_kv_indices(const wa_plan* plan, int g, int32_t* dst, size_t n);
+
+/*
+ * wa_plan_items -- copy the per-head work items to host memory: n_items rows of
+ * WA_ITEM_COLS int32 (columns named by WA_ITEM_*).  Every head runs the same items.
+ * WA_ERR_INVALID if n is too small.
+ */
+int wa_plan_items(const wa_plan* plan, int32_t* dst, size_t n);
+
+/* wa_last_error -- message of the calling thread's last non-zero status ("" if none). */
+const char* wa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WA_H_ */

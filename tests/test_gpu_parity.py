@@ -1,0 +1,158 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Tolerance (bf16 products, fp32 softmax and accumulation, output rounded to the input
+dtype): relative L2 error <= 5e-3 and max abs error <= 2e-2 against the oracle evaluated
+on the exact input values.  fp32 inputs are rounded to bf16 for the products, under the
+same bound.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from chunk_windowed_softmax_amd.workloads import WORKLOADS, make_custom_inputs, make_inputs
+from oracle import Geometry, window_attention_reference, window_attention_rows
+
+pytestmark = pytest.mark.gpu
+
+REL_L2 = 5e-3
+MAX_ABS = 2e-2
+
+
+def _say(msg):
+    print(f"[gpu-parity] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def _errors(got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    mx = np.abs(got - ref).max()
+    return rel, mx
+
+
+def _run(wa, w, q, k, v, out=None):
+    plan = wa.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, q.shape[1], q.shape[2])
+    o = wa.wa_forward(plan, q, k, v, out=out)
+    torch.cuda.synchronize()
+    return o
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "dense"])
+def test_full_parity(gpu_lib, name):
+    w = WORKLOADS[name]
+    _say(f"full parity {name}: T={w.T} S={w.S} G={w.G} K={w.K} r={w.radius} H={w.H} d={w.d} {w.dtype}")
+    q, k, v = make_inputs(w, seed=0)
+    ref = window_attention_reference(q, k, v, Geometry(*w.geometry))
+    out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda())
+    assert out.dtype == w.dtype and tuple(out.shape) == (w.L, w.H, w.d)
+    rel, mx = _errors(out.float().cpu(), ref)
+    _say(f"{name}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+def test_ragged_parity(gpu_lib):
+    w = WORKLOADS["ragged"]
+    _say("ragged parity (heads 0, 7, 15 in full; all heads on sampled rows)")
+    q, k, v = make_inputs(w, seed=0)
+    out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda()).float().cpu()
+    heads = [0, 7, 15]
+    ref = window_attention_reference(q[:, heads], k[:, heads], v[:, heads], Geometry(*w.geometry))
+    rel, mx = _errors(out[:, heads], ref)
+    _say(f"ragged heads {heads}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+    rng = np.random.default_rng(1)
+    rows = np.unique(np.concatenate([rng.choice(w.L, 48, replace=False), [0, w.T * w.S - 1, w.T * w.S, w.L - 1]]))
+    ref_rows = window_attention_rows(q, k, v, Geometry(*w.geometry), rows, range(w.H))
+    rel, mx = _errors(out[rows], ref_rows)
+    _say(f"ragged sampled rows: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+def _sample_rows(w, n, seed):
+    rng = np.random.default_rng(seed)
+    n_frame = w.T * w.S
+    edges = [0, w.S - 1, n_frame - 1, n_frame, w.L - 1]
+    chunk_rows = w.K * w.S
+    edges += [c * chunk_rows for c in range(1, 4)] + [c * chunk_rows - 1 for c in range(1, 4)]
+    picks = rng.choice(w.L, n, replace=False)
+    glob = n_frame + rng.choice(w.G, min(16, w.G), replace=False) if w.G else []
+    return np.unique(np.concatenate([picks, edges, glob]).astype(np.int64))
+
+
+@pytest.mark.parametrize("name", ["h3", "h3_full"])
+def test_h3_scale_sampled_parity(gpu_lib, name):
+    w = WORKLOADS[name]
+    _say(f"{name}: generating inputs L={w.L} H={w.H}")
+    q, k, v = make_inputs(w, seed=0)
+    _say(f"{name}: running")
+    out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda())
+    assert not torch.isnan(out).any()
+    out = out.cpu()
+    rows = _sample_rows(w, 96 if w.H <= 8 else 24, seed=2)
+    heads = list(range(w.H)) if w.H <= 8 else [0, 13, 27, 41, 55]
+    _say(f"{name}: oracle on {len(rows)} rows x {len(heads)} heads")
+    ref = window_attention_rows(q, k, v, Geometry(*w.geometry), rows, heads)
+    rel, mx = _errors(out[rows][:, heads].float(), ref)
+    _say(f"{name} sampled: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+@pytest.mark.parametrize("geom,H,d,dtype", [
+    ((1, 1, 0, 1, 0), 1, 64, torch.bfloat16),      # one row
+    ((3, 5, 1, 2, 0), 2, 128, torch.bfloat16),     # tiny ragged rows, one global
+    ((13, 7, 3, 5, 1), 3, 64, torch.float32),      # last chunk partial, fp32
+    ((9, 33, 130, 2, 3), 2, 128, torch.bfloat16),  # radius >= chunks with globals; 2 global tiles
+    ((11, 70, 65, 3, 1), 1, 128, torch.bfloat16),  # rows not a multiple of 32/64/128
+    ((40, 48, 200, 1, 2), 2, 64, torch.bfloat16),  # K = 1, many groups, split global leg
+])
+def test_edge_geometries(gpu_lib, geom, H, d, dtype):
+    T, S, G, K, r = geom
+    _say(f"edge geometry T={T} S={S} G={G} K={K} r={r} H={H} d={d} {dtype}")
+    L = T * S + G
+    q, k, v = make_custom_inputs(L, H, d, dtype, seed=3)
+    plan = gpu_lib.wa_plan_create(T, S, G, K, r, H, d)
+    out = gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    ref = window_attention_reference(q, k, v, Geometry(T, S, G, K, r))
+    rel, mx = _errors(out.float().cpu(), ref)
+    _say(f"rel_l2={rel:.3e} max_abs={mx:.3e} splits={plan.info['n_splits']}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+def test_cover_determinism_locality(gpu_lib):
+    """Every output element written (NaN prefill), bitwise repeatable, and keys outside a
+    row's window are never read (perturbing them leaves those rows bit-identical)."""
+    w = WORKLOADS["small"]
+    _say("cover / determinism / locality on small")
+    q, k, v = (x.cuda() for x in make_inputs(w, seed=4))
+    plan = gpu_lib.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
+    out1 = torch.full_like(q, float("nan"))
+    gpu_lib.wa_forward(plan, q, k, v, out=out1)
+    out2 = torch.full_like(q, float("nan"))
+    gpu_lib.wa_forward(plan, q, k, v, out=out2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out1).any()
+    assert torch.equal(out1, out2)
+    # chunk 0 (frames 0..2) sees chunks 0..1 = rows [0, 1536) plus globals
+    span_end = 2 * w.K * w.S
+    k2, v2 = k.clone(), v.clone()
+    k2[span_end:w.T * w.S] = 7.0
+    v2[span_end:w.T * w.S] = -7.0
+    out3 = gpu_lib.wa_forward(plan, q, k2, v2)
+    torch.cuda.synchronize()
+    first_chunk = w.K * w.S
+    assert torch.equal(out3[:first_chunk], out1[:first_chunk])
+    assert not torch.equal(out3[first_chunk:2 * first_chunk], out1[first_chunk:2 * first_chunk])
+
+
+def test_rows_sum_to_one_and_fp32_output(gpu_lib):
+    w = WORKLOADS["tiny"]
+    _say("ones-V on tiny (fp32)")
+    q, k, _ = make_inputs(w, seed=5)
+    v = torch.ones_like(q)
+    out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda())
+    assert out.dtype == torch.float32
+    assert (out - 1).abs().max().item() <= 4e-3
