@@ -31,6 +31,8 @@ def _parse():
     ap.add_argument("--workload", default="h3", help="workload name (h3, h3_full, small, ragged, dense)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-heads", type=int, default=1, help="heads of the workload the CPU oracle runs")
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="first run a plain device copy of q (known bytes) to calibrate HBM byte counters")
     return ap.parse_args()
 
 
@@ -98,6 +100,14 @@ def main() -> int:
     flop = info["kept_pairs_per_head"] * w.H * 4 * w.d
 
     stream = torch.cuda.current_stream(dev)
+    if args.calibration_copy:
+        # one read + one write of q.numel()*2 bytes per copy; profiled beside the attention
+        scratch = torch.empty_like(q)
+        for _ in range(3):
+            scratch.copy_(q)
+        torch.cuda.synchronize()
+        print(f"calibration copy: {q.numel() * q.element_size()} bytes read and written per copy", flush=True)
+        del scratch
     for _ in range(args.warmup):
         wa.wa_forward(plan, q, k, v, out=out, stream=stream)
     torch.cuda.synchronize()

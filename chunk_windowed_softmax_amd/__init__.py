@@ -65,6 +65,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m chunk_windowed_softmax_amd.build`")
+    # torch brings its own HIP runtime; load it first so that libwa.so binds to the same
+    # runtime instance as the tensors and streams it is handed.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32p = ctypes.POINTER(ctypes.c_int32)

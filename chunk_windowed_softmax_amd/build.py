@@ -20,7 +20,8 @@ ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for all device code; -O3, C++17, position independent.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
+          "-I", os.path.join(os.path.dirname(PKG), "include")]
 
 SOURCES = ["kernels.hip", "api.cpp", "plan.cpp"]
 

@@ -15,7 +15,7 @@
 #include <mutex>
 #include <string>
 
-#include "../../include/wa.h"
+#include "wa.h"
 #include "launch.h"
 #include "plan.h"
 
@@ -282,6 +282,7 @@ int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v
   a.L = h.L;
   a.G = h.geo.G;
   a.frame_rows = h.n_frame_rows;
+  a.block_m = h.block_m;
   a.items = r->items;
   a.n_items = (int)h.items.size();
   a.n_splits = h.n_splits;
