@@ -30,7 +30,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="h3", help="workload name (h3, h3_full, small, ragged, dense)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--cpu-heads", type=int, default=1, help="heads of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-heads", type=int, default=3, help="heads of the workload the CPU oracle runs")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain device copy of q (known bytes) to calibrate HBM byte counters")
     return ap.parse_args()
@@ -69,6 +69,21 @@ def cpu_baseline(w, q, k, v, heads: int) -> dict:
                   f"(all {w.L} rows), {dt:.1f} s wall",
         "seconds": round(dt, 3),
     }
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per launch of the attention kernel from the committed rocprofv3 counters
+    (profiles/attn_kernel_<workload>.json), or None when absent or taken on other source."""
+    from chunk_windowed_softmax_amd.rocprof_summary import kernel_source_sha256
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"attn_kernel_{workload}.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None, rec
+    return rec["traffic_bytes"], rec
 
 
 def main() -> int:
@@ -130,6 +145,11 @@ def main() -> int:
 
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (ms_mean * 1e-3) / 1e12
+    # Algorithmic HBM bytes: q, k, v read once and out written once, plus the global leg's
+    # fp32 partials (written once, read once by the merge).
+    elem = 2 if w.dtype == torch.bfloat16 else 4
+    algo_bytes = 4 * w.L * w.H * w.d * elem + 2 * info["workspace_bytes"]
+    traffic, traffic_rec = recorded_traffic(w.name)
     res = {
         "metric": "kept-pair TFLOP/s at the H3-scale window call on 1 MI355X",
         "value": round(value, 2),
@@ -159,7 +179,10 @@ def main() -> int:
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else int(traffic),
+            "algorithmic_bytes": int(algo_bytes),
+            "traffic_source": None if traffic_rec is None else
+            f"profiles/attn_kernel_{w.name}.md" + ("" if traffic is not None else " (stale: kernel changed)"),
         },
     }
     if not args.no_cpu_baseline:
