@@ -18,8 +18,12 @@ LIB = os.path.join(PKG, "libwa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-# Packed fp32 VALU forms are disabled for all device code; -O3, C++17, position independent.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed fp32 VALU forms are disabled for all device code.  Matrix-core accumulators are
+# kept in VGPRs (the accumulation registers then hold matrix operands), which avoids
+# per-iteration copies between the two register files.  No NaN is assumed in the device
+# arithmetic (inputs are finite; infinities are kept), so max() needs no NaN quieting.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form=1",
+                "-fno-honor-nans"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
           "-I", os.path.join(os.path.dirname(PKG), "include")]
 

@@ -6,31 +6,38 @@
 // the global rows, scattered into one contiguous output.
 //
 // Kernels
-//   attn_kernel     one work item = (block of up to 128 or 256 query rows, head, <= 2
-//                   key segments).  Both legs run in the same launch: window items read
-//                   their chunk span and then the global rows in place (no gathered
-//                   copy); global-leg items read one key split and write fp32 partials.
+//   attn_kernel     one work item = (block of up to 256 query rows, head, <= 2 key
+//                   segments).  Both legs run in the same launch: window items read their
+//                   chunk span and then the global rows in place (no gathered copy);
+//                   global-leg items read one key split and write fp32 partials.
 //   combine_kernel  log-sum-exp merge of the global leg's key splits into the output.
 //   f32_to_bf16     staging of fp32 inputs into bf16 for the matrix products.
 //
-// Attention mainloop (per wave: 32 query rows, all heads' rows are [L, H, d]):
+// Attention mainloop (4 waves per block, one per SIMD; per wave 64 query rows as two
+// 32-row blocks; all of q/k/v/out are [L, H, d]):
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = K tile rows (keys) from LDS, B = the
 //   wave's Q rows held in registers.  In the accumulator layout each lane then holds 16
 //   keys of ONE query per 32-key block, so the row max / row sum are in-lane reductions
-//   plus a single exchange with the lane 32 apart.
+//   plus a single exchange with the lane 32 apart (v_permlane32_swap).
 //   O^T += V^T P^T on the same instruction: B = P^T straight from the S^T accumulators
 //   (rounded to bf16), A = V^T read from the row-major V tile with ds_read_tr16_b64
-//   (LDS transpose read), so V needs no transposed copy anywhere.
+//   (LDS transpose read), so V needs no transposed copy anywhere.  Each K and V fragment
+//   read from LDS feeds the matrix ops of both 32-row blocks.
 //   Softmax runs in the log2 domain (exp2 with log2(e)/sqrt(d) folded into one FMA),
 //   online over 64-key tiles with fp32 running max / sum / accumulators.
-//   K/V tiles are double-buffered in LDS and filled by direct global->LDS 16-byte loads
-//   (no registers, no LDS write instructions): the next tile's loads are issued before
-//   the current tile's math, one barrier per tile.  LDS rows hold d bf16; 16-byte chunks
-//   are XOR-swizzled per row (applied on the global side of the DMA) so the K reads and
-//   the transpose reads are free of bank conflicts.
-//   The running max is raised lazily: the accumulators are rescaled only when some
-//   row's max grows by more than 2^8 (wave-uniform branch), otherwise exponentials are
-//   taken against the stale max (values up to 2^8, exact in the softmax ratio).
+//   The matrix ops of one tile come in four groups of 16 (S of block 0, PV of block 1 for
+//   the previous tile, S of block 1, PV of block 0); the exponentials, bf16 packing and
+//   row sums of the other block, and the LDS reads of the next fragments, are interleaved
+//   one matrix op at a time, so the vector ALU and LDS work hides under the matrix pipe.
+//   K/V tiles stream through a 4-deep LDS ring filled by direct global->LDS 16-byte loads
+//   (no registers, no LDS write instructions), issued three tiles ahead and spread over
+//   the matrix ops; one barrier per tile.  LDS rows hold d bf16; 16-byte chunks are
+//   XOR-swizzled per row (applied on the global side of the DMA) so the K reads and the
+//   transpose reads are free of bank conflicts.
+//   The running max is raised lazily: exponentials are taken against the running max,
+//   and a wave-uniform slow path raises it (rescaling the accumulators) only when some
+//   row's max grew by more than 2^8 (values up to 2^8 are exact in the softmax ratio);
+//   the same path masks keys past a segment end.
 //   Blocks are remapped so that consecutive work items (same head, same group, adjacent
 //   query tiles sharing all their keys) land on the same XCD and share its L2.
 #include <hip/hip_runtime.h>
@@ -51,7 +58,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kWaveRows = 32;  // query rows per wave
+constexpr int kNW = 4;         // waves per block, one per SIMD
+constexpr int kWaveRows = 64;  // query rows per wave (two 32-row blocks)
 constexpr int kBN = kBlockN;   // keys per tile
 static_assert(kBN == 64, "the fragment code below assumes 64-key tiles");
 
@@ -101,24 +109,38 @@ struct AttnParams {
   float scale_log2;
 };
 
-template <int D, int NW, bool OUT_F32>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void attn_kernel(AttnParams p) {
-  constexpr int NT = NW * 64;                   // threads per block
+// One block = 4 waves (one per SIMD); one wave = 64 query rows as two 32-row blocks
+// (qb = 0, 1).  Every K and V fragment read from LDS feeds both blocks' matrix ops.
+//
+// Per 64-key tile the wave runs four phases; each pairs matrix ops with independent
+// vector work so that the matrix pipe stays busy (ALU work issues while a matrix op runs):
+//   P1  S0 = K Q0^T
+//   P2  S1 = K Q1^T                 | softmax(S0) -> P0, transpose reads of the V tile
+//   P3  O0 += V^T P0^T              | softmax(S1) -> P1
+//   --  wait for the next tile's DMA, barrier, DMA of the tile after it into this buffer
+//   P4  O1 += V^T P1^T              | K fragment reads of the next tile, row sums of P0, P1
+// The exponentials of a tile are taken against the running max before the tile's own max
+// is known; a wave-uniform slow path redoes a query block when that max exceeds the
+// running one by more than 2^8 or when the tile has masked keys (segment end).
+template <int D, bool OUT_F32>
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_kernel(AttnParams p) {
   constexpr int CH = D / 8;                     // 16-byte chunks per row
   constexpr int ROWB = D * 2;                   // bytes per LDS row
   constexpr int TILEB = kBN * ROWB;             // bytes per K or V tile
   constexpr int NJ = TILEB / 1024;              // 1 KB DMA slices (one wave instruction) per tile
-  constexpr int JPW = NJ / NW;                  // slices per wave per tensor per tile
+  constexpr int JPW = NJ / kNW;                 // slices per wave per tensor per tile
   constexpr int KS = D / 16;                    // MFMA k-steps over d
   constexpr int DB = D / 32;                    // 32-wide output column blocks
-  static_assert(NJ % NW == 0, "tile slices must divide evenly over the waves");
+  static_assert(NJ % kNW == 0, "tile slices must divide evenly over the waves");
   constexpr float kLazyLog2 = 8.f;              // rescale only when the max grows by > 2^8
 
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILEB];  // K0 V0 K1 V1
+  constexpr int NBUF = 4;                       // LDS ring of (K, V) tile pairs
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * 2 * TILEB];  // K0 V0 K1 V1 ...
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;     // half of the wave: k sub-block of the MFMA operands
   const int l32 = lane & 31;
 
@@ -130,34 +152,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int H = p.H;
   const uint32_t row_bytes = uint32_t(H) * D * 2;  // bytes between consecutive rows of q/k/v
 
-  // ---- Q fragments of this wave (B operand of S^T = K Q^T): lane = query row, 8 d each
-  const int qrow = it.q_begin + wave * kWaveRows + l32;
-  const bool wave_active = it.q_begin + wave * kWaveRows < it.q_end;
-  bf16x8 qf[KS];
-  {
-    const bool ok = qrow < it.q_end;
-    const uint16_t* src = p.q + ((int64_t)qrow * H + h) * D + 8 * hh;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (ok) x = *reinterpret_cast<const u32x4*>(src + 16 * s);
-      qf[s] = __builtin_bit_cast(bf16x8, x);
-    }
-  }
+  // ---- Q fragments (B operand of S^T = K Q^T): lane = query row, 8 d each
+  const int row0 = it.q_begin + wave * kWaveRows;
+  const bool wave_active = row0 < it.q_end;
+  bf16x8 qf[2][KS];  // loaded in the prologue below, together with the first K/V tile
 
   // ---- DMA source offsets: LDS slice j holds tile rows [j*1024/ROWB, ...); lane writes LDS
   // chunk (j*64 + lane), i.e. row m/CH, physical chunk m%CH, which holds the logical chunk
   // (physical ^ swz(row)) of that key row.
-  uint32_t dma_off[JPW];
-  int dma_row[JPW];
-#pragma unroll
-  for (int i = 0; i < JPW; ++i) {
-    const int j = i * NW + wave;
-    const int m = j * 64 + lane;
-    const int row = m / CH, phys = m % CH;
-    dma_row[i] = row;
-    dma_off[i] = uint32_t(row) * row_bytes + uint32_t(h * D * 2) + uint32_t(((phys ^ swz<D>(row)) * 8) * 2);
-  }
+  // Slice i of a lane lies RPI rows below slice 0 and has the same swizzle (the swizzle
+  // depends on row % 16 and RPI is a multiple of 16), so one base offset serves all slices.
+  constexpr int RPI = kNW * 64 / CH;  // tile rows between consecutive slices of one wave
+  static_assert(RPI % 16 == 0, "slices of one lane must share the row swizzle");
+  const int dma_row0 = (wave * 64 + lane) / CH;
+  const uint32_t dma_off0 = uint32_t(dma_row0) * row_bytes + uint32_t(h * D * 2) +
+                            uint32_t((((wave * 64 + lane) % CH) ^ swz<D>(dma_row0)) * 16);
 
   // ---- LDS read offsets (bytes within a tile)
   uint32_t koff[KS];  // K fragment (key row l32 of a 32-key block, chunk 2s+hh)
@@ -180,7 +189,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
   const int nt0 = (it.kv0_end - it.kv0_begin + kBN - 1) / kBN;
   const int nt1 = (it.kv1_end - it.kv1_begin + kBN - 1) / kBN;
   const int nt = nt0 + nt1;
-  auto tile_range = [&](int t, int& n0, int& nend) {
+  auto tile_range = [&](int t, int& n0, int& nend) __attribute__((always_inline)) {
     if (t < nt0) {
       n0 = it.kv0_begin + t * kBN;
       nend = it.kv0_end;
@@ -190,181 +199,388 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
     }
   };
 
-  // Issue the DMA of tile t into buffer `buf`.  Rows past the segment end re-read the
+  // DMA load `idx` (slice idx / 2, K for even idx and V for odd) of tile u into ring slot
+  // u % NBUF.  Tiles past the last one re-load the last tile (into a slot nobody reads), so
+  // every tile issues the same number of loads.  Rows past the segment end re-read the
   // segment's last row (finite data, masked out of the softmax), so no key outside the
   // item's kept set is ever read.
-  auto issue_tile = [&](int t, int buf) {
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
+  auto dma_load = [&](int u, int idx) __attribute__((always_inline)) {
+    const int uu = u < nt ? u : nt - 1;
     int n0, nend;
-    tile_range(t, n0, nend);
-    const unsigned char* kg = reinterpret_cast<const unsigned char*>(p.k) + (int64_t)n0 * row_bytes;
-    const unsigned char* vg = reinterpret_cast<const unsigned char*>(p.v) + (int64_t)n0 * row_bytes;
-    unsigned char* kl = smem + (2 * buf) * TILEB;
-    unsigned char* vl = kl + TILEB;
+    tile_range(uu, n0, nend);
+    const int i = idx >> 1;
+    const unsigned char* g = reinterpret_cast<const unsigned char*>((idx & 1) ? p.v : p.k) + (int64_t)n0 * row_bytes;
+    const uint32_t l = lds_base + uint32_t((2 * (u % NBUF) + (idx & 1)) * TILEB + (i * kNW + wave) * 1024);
     const int last = nend - 1 - n0;
-#pragma unroll
-    for (int i = 0; i < JPW; ++i) {
-      const int j = i * NW + wave;
-      uint32_t off = dma_off[i];
-      if (last < kBN - 1 && dma_row[i] > last) off -= uint32_t(dma_row[i] - last) * row_bytes;
-      __builtin_amdgcn_global_load_lds(kg + off, (lds_void*)(kl + j * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vg + off, (lds_void*)(vl + j * 1024), 16, 0, 0);
-    }
+    const int row = dma_row0 + i * RPI;
+    uint32_t off = dma_off0 + uint32_t(i * RPI) * row_bytes;
+    if (last < kBN - 1 && row > last) off -= uint32_t(row - last) * row_bytes;
+    // Issued as asm: the compiler would otherwise make the next LDS read of any buffer wait
+    // for every DMA in flight (it cannot tell the ring slots apart).  Completion is ordered
+    // by the explicit vmcnt waits before each barrier.  M0 holds the LDS destination.
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :
+                 : "s"(l), "v"(off), "s"(g)
+                 : "memory", "m0");
   };
-
-  float m_run = -__builtin_inff();  // running max of raw scores (this lane's query)
-  float mc = 0.f;                   // m_run * c2
-  float l_run0 = 0.f, l_run1 = 0.f;  // this lane's half of the running sum (two chains)
-  f32x16 oacc[DB];
-#pragma unroll
-  for (int db = 0; db < DB; ++db)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[db][i] = 0.f;
+  constexpr int NLD = 2 * JPW;  // DMA loads per tile per wave
 
   const float c2 = p.scale_log2;
   const float lazy_raw = kLazyLog2 / c2;
 
-  issue_tile(0, 0);
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  __syncthreads();
-
-  for (int t = 0; t < nt; ++t) {
-    const int cur = t & 1;
-    if (t + 1 < nt) issue_tile(t + 1, cur ^ 1);
-
-    if (wave_active) {
-      const unsigned char* kb = smem + (2 * cur) * TILEB;
-      const unsigned char* vb = kb + TILEB;
-
-      // S^T[key][query] for the two 32-key blocks of the tile
-      f32x16 sacc[2];
+  float m_run[2], mc[2], l_run[2];  // running max of raw scores (this lane's queries), * c2, sum
+  f32x16 oacc[2][DB];
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[b][i] = 0.f;
-#pragma unroll
-      for (int s = 0; s < KS; ++s)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const u32x4 x = *reinterpret_cast<const u32x4*>(kb + koff[s] + b * 32 * ROWB);
-          sacc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, x), qf[s], sacc[b], 0, 0, 0);
-        }
-
-      // mask keys past the segment end (only the last tile of a segment)
-      int n0, nend;
-      tile_range(t, n0, nend);
-      const int valid = nend - n0;
-      if (valid < kBN) {
-#pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = b * 32 + (i >> 2) * 8 + 4 * hh + (i & 3);
-            if (key >= valid) sacc[b][i] = -__builtin_inff();
-          }
-      }
-
-      // online softmax (log2 domain) with lazy rescaling
-      float mt = sacc[0][0];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sacc[b][i]);
-      mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
-      if (__builtin_amdgcn_ballot_w64(mt > m_run + lazy_raw) != 0) {
-        const float m_new = __builtin_fmaxf(m_run, mt);
-        const float alpha = fast_exp2((m_run - m_new) * c2);
-        m_run = m_new;
-        mc = m_new * c2;
-        l_run0 *= alpha;
-        l_run1 *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
-      }
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[b][i] = fast_exp2(__builtin_fmaf(sacc[b][i], c2, -mc));
-
-      // O^T += V^T P^T.  P is rounded to bf16 for the product, and the row sum adds up
-      // exactly those rounded values (v_dot2 with (1, 1)), so the weights applied to V sum
-      // to one and a row dominated by one key reproduces that key's value.
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          const bf16x2 p0 = cvt_bf16x2(sacc[b][8 * tt + 0], sacc[b][8 * tt + 1]);
-          const bf16x2 p1 = cvt_bf16x2(sacc[b][8 * tt + 2], sacc[b][8 * tt + 3]);
-          const bf16x2 p2 = cvt_bf16x2(sacc[b][8 * tt + 4], sacc[b][8 * tt + 5]);
-          const bf16x2 p3 = cvt_bf16x2(sacc[b][8 * tt + 6], sacc[b][8 * tt + 7]);
-          l_run0 = __builtin_amdgcn_fdot2_f32_bf16(p0, kOnes2, l_run0, false);
-          l_run1 = __builtin_amdgcn_fdot2_f32_bf16(p1, kOnes2, l_run1, false);
-          l_run0 = __builtin_amdgcn_fdot2_f32_bf16(p2, kOnes2, l_run0, false);
-          l_run1 = __builtin_amdgcn_fdot2_f32_bf16(p3, kOnes2, l_run1, false);
-          const bf16x8 pf = __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
-                                                    __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5, 6, 7);
-          const unsigned char* vt = vb + (32 * b + 16 * tt) * ROWB;
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const i16x4 r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db][0]));
-            const i16x4 r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db][1]));
-            const u32x4 vw = {__builtin_bit_cast(u32x2, r0)[0], __builtin_bit_cast(u32x2, r0)[1],
-                              __builtin_bit_cast(u32x2, r1)[0], __builtin_bit_cast(u32x2, r1)[1]};
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vw), pf, oacc[db], 0, 0, 0);
-          }
-        }
-      }
-    }
-
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the next tile's DMA has landed in LDS
-    __syncthreads();
-  }
-
-  if (!wave_active) return;
-  const float l_run = l_run0 + l_run1;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (qrow >= it.q_end) return;
-
-  if (it.split < 0) {
-    const float inv = 1.f / l_tot;
-    if constexpr (OUT_F32) {
-      float* orow = reinterpret_cast<float*>(p.out) + ((int64_t)qrow * H + h) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int dv = 32 * db + 8 * g4 + 4 * hh;
-          const f32x4 o = {oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv, oacc[db][4 * g4 + 2] * inv,
-                           oacc[db][4 * g4 + 3] * inv};
-          *reinterpret_cast<f32x4*>(orow + dv) = o;
-        }
-    } else {
-      uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)qrow * H + h) * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int dv = 32 * db + 8 * g4 + 4 * hh;
-          const u32x2 o = {pack_bf16x2(oacc[db][4 * g4] * inv, oacc[db][4 * g4 + 1] * inv),
-                           pack_bf16x2(oacc[db][4 * g4 + 2] * inv, oacc[db][4 * g4 + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + dv) = o;
-        }
-    }
-  } else {
-    const int64_t slot = ((int64_t)it.split * p.G + (qrow - p.frame_rows)) * H + h;
-    float* po = p.part_o + slot * D;
+  for (int qb = 0; qb < 2; ++qb) {
+    m_run[qb] = -__builtin_inff();
+    mc[qb] = 0.f;
+    l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dv = 32 * db + 8 * g4 + 4 * hh;
-        const f32x4 o = {oacc[db][4 * g4], oacc[db][4 * g4 + 1], oacc[db][4 * g4 + 2], oacc[db][4 * g4 + 3]};
-        *reinterpret_cast<f32x4*>(po + dv) = o;
+      for (int i = 0; i < 16; ++i) oacc[qb][db][i] = 0.f;
+  }
+
+  bf16x8 kf[KS][2];        // K fragments of the current tile: [k-step][32-key block]
+  i16x4 vr[4 * DB][2];     // V^T fragments as transpose-read halves: [(b*2+tt)*DB+db][half]
+  bf16x2 pw[2][16];        // P^T as bf16 pairs: [qb][pair]; pair n = b*8 + tt*4 + k holds
+                           // S elements (b, 8*tt + 2*k + {0, 1}) of this lane
+  float mt_acc[2];         // running tile max of raw scores while P is formed
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int n = 0; n < 16; ++n) pw[qb][n] = cvt_bf16x2(0.f, 0.f);
+
+  auto read_k = [&](const unsigned char* kb, int idx) __attribute__((always_inline)) {
+    const int s = idx >> 1, b = idx & 1;
+    kf[s][b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + koff[s] + b * 32 * ROWB));
+  };
+  auto read_v = [&](const unsigned char* vb, int idx) __attribute__((always_inline)) {
+    const int f = idx >> 1, rr = idx & 1;
+    const int b = f / (2 * DB), tt = (f / DB) & 1, db = f % DB;
+    const unsigned char* vt = vb + (32 * b + 16 * tt) * ROWB;
+    vr[f][rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db][rr]));
+  };
+  auto vfrag = [&](int b, int tt, int db) __attribute__((always_inline)) -> bf16x8 {
+    const int f = (b * 2 + tt) * DB + db;
+    const u32x4 vw = {__builtin_bit_cast(u32x2, vr[f][0])[0], __builtin_bit_cast(u32x2, vr[f][0])[1],
+                      __builtin_bit_cast(u32x2, vr[f][1])[0], __builtin_bit_cast(u32x2, vr[f][1])[1]};
+    return __builtin_bit_cast(bf16x8, vw);
+  };
+  auto pfrag = [&](int qb, int b, int tt) __attribute__((always_inline)) -> bf16x8 {
+    const int n = b * 8 + tt * 4;
+    return __builtin_shufflevector(__builtin_shufflevector(pw[qb][n], pw[qb][n + 1], 0, 1, 2, 3),
+                                   __builtin_shufflevector(pw[qb][n + 2], pw[qb][n + 3], 0, 1, 2, 3), 0, 1, 2, 3,
+                                   4, 5, 6, 7);
+  };
+  // One pair of P against the given max (raw-score max tracked on the side).
+  auto p_pair = [&](int qb, const f32x16 (&sa)[2], int n, float mcq) __attribute__((always_inline)) {
+    const int b = n >> 3, e = 2 * (n & 7);
+    const float x0 = sa[b][e], x1 = sa[b][e + 1];
+    mt_acc[qb] = __builtin_fmaxf(mt_acc[qb], __builtin_fmaxf(x0, x1));
+    pw[qb][n] = cvt_bf16x2(fast_exp2(__builtin_fmaf(x0, c2, -mcq)), fast_exp2(__builtin_fmaf(x1, c2, -mcq)));
+  };
+  // Value of the lane 32 apart (the other half of the same query's keys), in both orders.
+  auto other_half = [](float x) __attribute__((always_inline)) -> f32x2 {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    return f32x2{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+  };
+  // max over both halves of the wave: {own, other} in some order per lane
+  auto pair_max = [&](float x) __attribute__((always_inline)) -> float {
+    const f32x2 r = other_half(x);
+    return __builtin_fmaxf(r[0], r[1]);
+  };
+  // Keeps the fast-path P computed ahead of the slow-path branch (and so inside the phase
+  // whose matrix ops hide it): an empty asm that reads it.
+  auto pin_p = [&](int qb) __attribute__((always_inline)) {
+    asm volatile("" ::"v"(pw[qb][0]), "v"(pw[qb][1]), "v"(pw[qb][2]), "v"(pw[qb][3]), "v"(pw[qb][4]),
+                 "v"(pw[qb][5]), "v"(pw[qb][6]), "v"(pw[qb][7]), "v"(pw[qb][8]), "v"(pw[qb][9]), "v"(pw[qb][10]),
+                 "v"(pw[qb][11]), "v"(pw[qb][12]), "v"(pw[qb][13]), "v"(pw[qb][14]), "v"(pw[qb][15]));
+  };
+  // Slow path of one query block (wave-uniform): mask keys past the segment end, raise the
+  // running max (rescaling the accumulators) when it grew by more than 2^8, redo P.
+  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid) __attribute__((always_inline)) {
+    if (valid < kBN) {
+      const int lim = valid - 4 * hh;  // key (b*32 + (i/4)*8 + 4*hh + i%4) >= valid
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sa[b][i] = (b * 32 + (i >> 2) * 8 + (i & 3)) >= lim ? -__builtin_inff() : sa[b][i];
+    }
+    float mt = sa[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
+    mt = pair_max(mt);
+    if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + lazy_raw) != 0) {
+      const float m_new = __builtin_fmaxf(m_run[qb], mt);
+      const float alpha = fast_exp2((m_run[qb] - m_new) * c2);
+      m_run[qb] = m_new;
+      mc[qb] = m_new * c2;
+      l_run[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
+    }
+#pragma unroll
+    for (int n = 0; n < 16; ++n) p_pair(qb, sa, n, mc[qb]);
+  };
+  // Row sums of exactly the rounded P that multiplied V (v_dot2 with (1, 1)), so the weights
+  // applied to V sum to one; two accumulation chains per block.
+  float rs[2][2];
+
+  // ---- Software pipeline over 64-key tiles, one "slot" = one group of matrix ops with a
+  // share of the vector work that is independent of them:
+  //   slot 0: S0(t) = K(t) Q0^T          | P1(t-1) pairs 8..15, 2nd half of the DMA of t+2;
+  //                                        then the check of block 1 (tile t-1)
+  //   slot 1: O1 += V(t-1)^T P1(t-1)^T   | P0(t) pairs 0..7, row sums of P1(t-1), V(t)
+  //                                        transpose reads (each fragment right after its
+  //                                        last use by this slot)
+  //   slot 2: S1(t) = K(t) Q1^T          | P0(t) pairs 8..15; then the check of block 0
+  //   barrier: tile t+1 has landed for every wave
+  //   slot 3: O0 += V(t)^T P0(t)^T       | P1(t) pairs 0..7, K(t+1) reads, row sums of P0(t),
+  //                                        1st half of the DMA of t+3
+  // The LDS ring has 4 slots: the DMA of t+3 overwrites tile t-1, whose reads every wave
+  // finished before the barrier of tile t.  Before the first tile, block 1's "previous tile"
+  // is empty (scores -inf, V zero), so every iteration runs the same code; block 1's last
+  // PV runs after the loop.
+  // P pairs are staged: pair k's FMAs issue at step fs(k), its exponentials one step later
+  // and its bf16 packing one step after that, so no vector op waits on the one before it.
+  constexpr int NS = 2 * KS;                // matrix ops of an S slot
+  constexpr int NP = 4 * DB;                // matrix ops of a PV slot
+  static_assert(NS % 4 == 0 && NP % 4 == 0 && (2 * KS) % NP == 0 && 16 % NP == 0 && NLD % 2 == 0,
+                "slot work must divide evenly over the steps");
+  f32x16 s0[2], s1[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s1[b][i] = -__builtin_inff();
+#pragma unroll
+  for (int f = 0; f < 4 * DB; ++f) vr[f][0] = vr[f][1] = i16x4{0, 0, 0, 0};
+  mt_acc[0] = mt_acc[1] = -__builtin_inff();
+  const f32x16 zero = {};
+  float fa[8], fb[8];  // staged pair values
+
+  // stage work of pairs [lo, lo + 8) of block qb at step i of an N-step slot
+  auto stage_at = [&](int qb, const f32x16 (&sa)[2], int lo, int N, int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int fs = k * N / 8;
+      const int n = lo + k, b = n >> 3, e = 2 * (n & 7);
+      if (fs + 2 == i) pw[qb][n] = cvt_bf16x2(fa[k], fb[k]);
+      if (fs + 1 == i) {
+        fa[k] = fast_exp2(fa[k]);
+        fb[k] = fast_exp2(fb[k]);
       }
-    if (hh == 0) {
-      const float2 ml = make_float2(m_run * c2, l_tot);
-      *reinterpret_cast<float2*>(p.part_ml + slot * 2) = ml;
+      if (fs == i) {
+        const float x0 = sa[b][e], x1 = sa[b][e + 1];
+        mt_acc[qb] = __builtin_fmaxf(mt_acc[qb], __builtin_fmaxf(x0, x1));
+        fa[k] = __builtin_fmaf(x0, c2, -mc[qb]);
+        fb[k] = __builtin_fmaf(x1, c2, -mc[qb]);
+      }
+    }
+  };
+  auto rows_at = [&](int qb, int steps, int i) __attribute__((always_inline)) {
+#pragma unroll
+    for (int k = i * 16 / steps; k < (i + 1) * 16 / steps; ++k)
+      rs[qb][k & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[qb][k], kOnes2, rs[qb][k & 1], false);
+  };
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid) __attribute__((always_inline)) {
+    pin_p(qb);
+    asm volatile("" ::"v"(mt_acc[qb]));
+    if (valid < kBN || __builtin_amdgcn_ballot_w64(pair_max(mt_acc[qb]) > m_run[qb] + lazy_raw) != 0)
+      slow_block(qb, sa, valid);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // PV slot of block qb: N matrix ops (when `mma`), then two tail steps for the staged pairs.
+  auto pv_slot = [&](int qb, bool mma, auto&& extra) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NP + 2; ++i) {
+      if (mma && i < NP) {
+        const int b = i / (2 * DB), tt = (i / DB) & 1, db = i % DB;
+        oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(b, tt, db), pfrag(qb, b, tt), oacc[qb][db], 0, 0, 0);
+      }
+      extra(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto s_slot = [&](int qb, f32x16 (&sa)[2], bool mma, auto&& extra) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NS + 2; ++i) {
+      if (mma && i < NS) {
+        const int st = i >> 1, b = i & 1;
+        sa[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st][b], qf[qb][st], st == 0 ? zero : sa[b], 0, 0, 0);
+      }
+      extra(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // s_waitcnt with vmcnt = n (n < 16) and the other counters at their maximum
+#define WA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
+
+  // prologue: tile 0 and the Q fragments land together (the explicit wait also tells the
+  // compiler that Q is complete, so it adds no wait inside the loop); then tiles 1 and the
+  // first half of 2 go in flight.
+#pragma unroll
+  for (int idx = 0; idx < NLD; ++idx) dma_load(0, idx);
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = row0 + 32 * qb + l32;
+    const bool ok = qrow < it.q_end;
+    const uint16_t* src = p.q + ((int64_t)qrow * H + h) * D + 8 * hh;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (ok) x = *reinterpret_cast<const u32x4*>(src + 16 * s);
+      qf[qb][s] = __builtin_bit_cast(bf16x8, x);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+#pragma unroll
+  for (int idx = 0; idx < NLD; ++idx) dma_load(1, idx);
+#pragma unroll
+  for (int idx = 0; idx < NLD / 2; ++idx) dma_load(2, idx);
+  barrier();
+  if (wave_active) {
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) read_k(smem, i);
+  }
+
+  int valid_prev = kBN;
+  for (int t = 0; t < nt; ++t) {
+    const unsigned char* vb = smem + (2 * (t % NBUF) + 1) * TILEB;
+    const unsigned char* kb_next = smem + (2 * ((t + 1) % NBUF)) * TILEB;
+    int n0, nend;
+    tile_range(t, n0, nend);
+    const int valid = nend - n0;
+
+    if (wave_active) {
+      // slot 0
+      s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
+        stage_at(1, s1, 8, NS, i);
+        if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)));
+      });
+      check_block(1, s1, valid_prev);
+      // slot 1
+      rs[1][0] = rs[1][1] = 0.f;
+      mt_acc[0] = -__builtin_inff();
+      pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
+        if (i < NP) {
+          read_v(vb, 2 * i);
+          read_v(vb, 2 * i + 1);
+        }
+        stage_at(0, s0, 0, NP, i);
+        if (i < NP) rows_at(1, NP, i);
+      });
+      asm volatile("" ::"v"(rs[1][0]), "v"(rs[1][1]));
+      l_run[1] += rs[1][0] + rs[1][1];
+      // slot 2
+      s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
+      check_block(0, s0, valid);
+    } else {
+#pragma unroll
+      for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx);
+    }
+
+    WA_WAIT_VMCNT(NLD);  // tile t+1 has landed (tile t+2 may still be in flight) ...
+    barrier();           // ... for every wave
+
+    if (wave_active) {
+      // slot 3 (after the last tile the K reads hit a buffer nobody uses)
+      rs[0][0] = rs[0][1] = 0.f;
+      mt_acc[1] = -__builtin_inff();
+      pv_slot(0, true, [&](int i) __attribute__((always_inline)) {
+        if (i < NP) {
+#pragma unroll
+          for (int r = 0; r < 2 * KS / NP; ++r) read_k(kb_next, i * (2 * KS / NP) + r);
+          rows_at(0, NP, i);
+          if (i % (NP / (NLD / 2)) == 0) dma_load(t + 3, i / (NP / (NLD / 2)));
+        }
+        stage_at(1, s1, 0, NP, i);
+      });
+      asm volatile("" ::"v"(rs[0][0]), "v"(rs[0][1]));
+      l_run[0] += rs[0][0] + rs[0][1];
+    } else {
+#pragma unroll
+      for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx);
+    }
+    valid_prev = valid;
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no DMA may still write this block's LDS at exit
+  if (wave_active) {  // block 1 of the last tile
+    s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { stage_at(1, s1, 8, NS, i); });
+    check_block(1, s1, valid_prev);
+    rs[1][0] = rs[1][1] = 0.f;
+    pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
+      if (i < NP) rows_at(1, NP, i);
+    });
+    l_run[1] += rs[1][0] + rs[1][1];
+  }
+#undef WA_WAIT_VMCNT
+
+  if (!wave_active) return;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = row0 + 32 * qb + l32;
+    const float l_tot = [&] {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, l_run[qb]),
+                                                      __builtin_bit_cast(uint32_t, l_run[qb]), false, false);
+      return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+    }();
+    if (qrow >= it.q_end) continue;
+    if (it.split < 0) {
+      const float inv = 1.f / l_tot;
+      if constexpr (OUT_F32) {
+        float* orow = reinterpret_cast<float*>(p.out) + ((int64_t)qrow * H + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dv = 32 * db + 8 * g4 + 4 * hh;
+            const f32x4 o = {oacc[qb][db][4 * g4] * inv, oacc[qb][db][4 * g4 + 1] * inv,
+                             oacc[qb][db][4 * g4 + 2] * inv, oacc[qb][db][4 * g4 + 3] * inv};
+            *reinterpret_cast<f32x4*>(orow + dv) = o;
+          }
+      } else {
+        uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)qrow * H + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dv = 32 * db + 8 * g4 + 4 * hh;
+            const u32x2 o = {pack_bf16x2(oacc[qb][db][4 * g4] * inv, oacc[qb][db][4 * g4 + 1] * inv),
+                             pack_bf16x2(oacc[qb][db][4 * g4 + 2] * inv, oacc[qb][db][4 * g4 + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + dv) = o;
+          }
+      }
+    } else {
+      const int64_t slot = ((int64_t)it.split * p.G + (qrow - p.frame_rows)) * H + h;
+      float* po = p.part_o + slot * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int dv = 32 * db + 8 * g4 + 4 * hh;
+          const f32x4 o = {oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
+                           oacc[qb][db][4 * g4 + 3]};
+          *reinterpret_cast<f32x4*>(po + dv) = o;
+        }
+      if (hh == 0) {
+        const float2 ml = make_float2(m_run[qb] * c2, l_tot);
+        *reinterpret_cast<float2*>(p.part_ml + slot * 2) = ml;
+      }
     }
   }
 }
@@ -412,7 +628,7 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
   }
 }
 
-template <int D, int NW, bool OUT_F32>
+template <int D, bool OUT_F32>
 hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   AttnParams p;
   p.q = static_cast<const uint16_t*>(a.q);
@@ -430,7 +646,7 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   p.per_xcd = (p.total + kXcds - 1) / kXcds;
   p.scale_log2 = a.scale_log2;
   const int grid = p.per_xcd * kXcds;
-  hipLaunchKernelGGL((attn_kernel<D, NW, OUT_F32>), dim3(grid), dim3(NW * 64), 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<D, OUT_F32>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_splits > 1) {
@@ -441,20 +657,12 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   return e;
 }
 
-template <int D, bool OUT_F32>
-hipError_t launch_rows(const ForwardArgs& a, hipStream_t stream) {
-  switch (a.block_m) {
-    case 128: return launch_typed<D, 4, OUT_F32>(a, stream);
-    case 256: return launch_typed<D, 8, OUT_F32>(a, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
 }  // namespace
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
-  if (a.d == 128) return a.out_f32 ? launch_rows<128, true>(a, stream) : launch_rows<128, false>(a, stream);
-  if (a.d == 64) return a.out_f32 ? launch_rows<64, true>(a, stream) : launch_rows<64, false>(a, stream);
+  if (a.block_m != kNW * kWaveRows) return hipErrorInvalidValue;
+  if (a.d == 128) return a.out_f32 ? launch_typed<128, true>(a, stream) : launch_typed<128, false>(a, stream);
+  if (a.d == 64) return a.out_f32 ? launch_typed<64, true>(a, stream) : launch_typed<64, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -16,7 +16,7 @@ struct ForwardArgs {
   void* out;              // [L, H, d], bf16 or fp32 (out_f32)
   bool out_f32;
   int d, H, L, G, frame_rows;
-  int block_m;            // query rows per work item: 128 (4 waves) or 256 (8 waves)
+  int block_m;            // query rows per work item: 256 (4 waves x 64 rows)
   const Item* items;      // device copy of the plan's items
   int n_items;
   int n_splits;           // > 1: global-leg items write partials, then a combine pass

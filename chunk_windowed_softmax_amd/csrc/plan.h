@@ -44,7 +44,7 @@ struct HostPlan {
   int64_t partial_bytes = 0;  // device workspace of the global leg's partial results
 };
 
-constexpr int kBlockM = 256;  // query rows per work item: 8 waves x 32 rows
+constexpr int kBlockM = 256;  // query rows per work item: 4 waves x 64 rows
 constexpr int kBlockN = 64;   // keys per staged K/V tile
 
 // Status codes mirror the C ABI (0 ok, 1 invalid, 2 unsupported).
