@@ -134,6 +134,7 @@ void attn_kernel(AttnParams p) {
   constexpr int DB = D / 32;                    // 32-wide output column blocks
   static_assert(NJ % kNW == 0, "tile slices must divide evenly over the waves");
   constexpr float kLazyLog2 = 8.f;              // rescale only when the max grows by > 2^8
+  constexpr float kRowSumLimit = 256.f;         // fast path only while this lane's row sum <= 2^8
 
   constexpr int NBUF = 4;                       // LDS ring of (K, V) tile pairs
   __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * 2 * TILEB];  // K0 V0 K1 V1 ...
@@ -164,9 +165,9 @@ void attn_kernel(AttnParams p) {
   // depends on row % 16 and RPI is a multiple of 16), so one base offset serves all slices.
   constexpr int RPI = kNW * 64 / CH;  // tile rows between consecutive slices of one wave
   static_assert(RPI % 16 == 0, "slices of one lane must share the row swizzle");
-  const int dma_row0 = (wave * 64 + lane) / CH;
-  const uint32_t dma_off0 = uint32_t(dma_row0) * row_bytes + uint32_t(h * D * 2) +
-                            uint32_t((((wave * 64 + lane) % CH) ^ swz<D>(dma_row0)) * 16);
+  const uint32_t dma_row0 = uint32_t((wave * 64 + lane) / CH);
+  // the lane's byte offset within a key row: head, then the swizzled 16-byte chunk
+  const uint32_t dma_lane = uint32_t(h * D * 2) + uint32_t((((wave * 64 + lane) % CH) ^ swz<D>(dma_row0)) * 16);
 
   // ---- LDS read offsets (bytes within a tile)
   uint32_t koff[KS];  // K fragment (key row l32 of a 32-key block, chunk 2s+hh)
@@ -212,17 +213,15 @@ void attn_kernel(AttnParams p) {
     const int i = idx >> 1;
     const unsigned char* g = reinterpret_cast<const unsigned char*>((idx & 1) ? p.v : p.k) + (int64_t)n0 * row_bytes;
     const uint32_t l = lds_base + uint32_t((2 * (u % NBUF) + (idx & 1)) * TILEB + (i * kNW + wave) * 1024);
-    const int last = nend - 1 - n0;
-    const int row = dma_row0 + i * RPI;
-    uint32_t off = dma_off0 + uint32_t(i * RPI) * row_bytes;
-    if (last < kBN - 1 && row > last) off -= uint32_t(row - last) * row_bytes;
+    // rows past the segment end re-read its last row (branch-free; 24-bit multiply)
+    const uint32_t last = uint32_t(nend - 1 - n0 < kBN - 1 ? nend - 1 - n0 : kBN - 1);
+    const uint32_t row = dma_row0 + uint32_t(i * RPI);
+    const uint32_t off = dma_lane + __umul24(row < last ? row : last, row_bytes);
     // Issued as asm: the compiler would otherwise make the next LDS read of any buffer wait
     // for every DMA in flight (it cannot tell the ring slots apart).  Completion is ordered
-    // by the explicit vmcnt waits before each barrier.  M0 holds the LDS destination.
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
-                 :
-                 : "s"(l), "v"(off), "s"(g)
-                 : "memory", "m0");
+    // by the explicit vmcnt waits before each barrier.  M0 holds the LDS destination (set
+    // by the compiler through the operand; the nop covers the M0-write-to-DMA hazard).
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(g), "{m0}"(l) : "memory");
   };
   constexpr int NLD = 2 * JPW;  // DMA loads per tile per wave
 
@@ -246,7 +245,6 @@ void attn_kernel(AttnParams p) {
   i16x4 vr[4 * DB][2];     // V^T fragments as transpose-read halves: [(b*2+tt)*DB+db][half]
   bf16x2 pw[2][16];        // P^T as bf16 pairs: [qb][pair]; pair n = b*8 + tt*4 + k holds
                            // S elements (b, 8*tt + 2*k + {0, 1}) of this lane
-  float mt_acc[2];         // running tile max of raw scores while P is formed
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
@@ -274,11 +272,13 @@ void attn_kernel(AttnParams p) {
                                    __builtin_shufflevector(pw[qb][n + 2], pw[qb][n + 3], 0, 1, 2, 3), 0, 1, 2, 3,
                                    4, 5, 6, 7);
   };
-  // One pair of P against the given max (raw-score max tracked on the side).
+  // Row sums of exactly the rounded P that multiplies V (v_dot2 with (1, 1)), so the
+  // weights applied to V sum to one; two accumulation chains per block, this lane's keys.
+  float rs[2][2];
+  // One pair of P against the given max.
   auto p_pair = [&](int qb, const f32x16 (&sa)[2], int n, float mcq) __attribute__((always_inline)) {
     const int b = n >> 3, e = 2 * (n & 7);
     const float x0 = sa[b][e], x1 = sa[b][e + 1];
-    mt_acc[qb] = __builtin_fmaxf(mt_acc[qb], __builtin_fmaxf(x0, x1));
     pw[qb][n] = cvt_bf16x2(fast_exp2(__builtin_fmaf(x0, c2, -mcq)), fast_exp2(__builtin_fmaf(x1, c2, -mcq)));
   };
   // Value of the lane 32 apart (the other half of the same query's keys), in both orders.
@@ -300,7 +300,8 @@ void attn_kernel(AttnParams p) {
                  "v"(pw[qb][11]), "v"(pw[qb][12]), "v"(pw[qb][13]), "v"(pw[qb][14]), "v"(pw[qb][15]));
   };
   // Slow path of one query block (wave-uniform): mask keys past the segment end, raise the
-  // running max (rescaling the accumulators) when it grew by more than 2^8, redo P.
+  // running max (rescaling the accumulators) when it grew by more than 2^8, redo P and its
+  // row sums.
   auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid) __attribute__((always_inline)) {
     if (valid < kBN) {
       const int lim = valid - 4 * hh;  // key (b*32 + (i/4)*8 + 4*hh + i%4) >= valid
@@ -327,12 +328,13 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[qb][db][i] *= alpha;
     }
+    rs[qb][0] = rs[qb][1] = 0.f;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) p_pair(qb, sa, n, mc[qb]);
+    for (int n = 0; n < 16; ++n) {
+      p_pair(qb, sa, n, mc[qb]);
+      rs[qb][n & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[qb][n], kOnes2, rs[qb][n & 1], false);
+    }
   };
-  // Row sums of exactly the rounded P that multiplied V (v_dot2 with (1, 1)), so the weights
-  // applied to V sum to one; two accumulation chains per block.
-  float rs[2][2];
 
   // ---- Software pipeline over 64-key tiles, one "slot" = one group of matrix ops with a
   // share of the vector work that is independent of them:
@@ -349,8 +351,12 @@ void attn_kernel(AttnParams p) {
   // finished before the barrier of tile t.  Before the first tile, block 1's "previous tile"
   // is empty (scores -inf, V zero), so every iteration runs the same code; block 1's last
   // PV runs after the loop.
-  // P pairs are staged: pair k's FMAs issue at step fs(k), its exponentials one step later
-  // and its bf16 packing one step after that, so no vector op waits on the one before it.
+  // P pairs are staged: pair k's FMAs issue at step fs(k), its exponentials one step later,
+  // its bf16 packing one step after that and its row-sum dot one more step later, so no
+  // vector op waits on the one before it.
+  // The fast path needs no tile max: any P above 2^8 (a score more than 2^8 above the
+  // running max, in exp2 units) makes this lane's row sum exceed 2^8, and that (or the first
+  // tile, or a masked tile) sends the block to the slow path, which finds the max.
   constexpr int NS = 2 * KS;                // matrix ops of an S slot
   constexpr int NP = 4 * DB;                // matrix ops of a PV slot
   static_assert(NS % 4 == 0 && NP % 4 == 0 && (2 * KS) % NP == 0 && 16 % NP == 0 && NLD % 2 == 0,
@@ -362,7 +368,7 @@ void attn_kernel(AttnParams p) {
     for (int i = 0; i < 16; ++i) s1[b][i] = -__builtin_inff();
 #pragma unroll
   for (int f = 0; f < 4 * DB; ++f) vr[f][0] = vr[f][1] = i16x4{0, 0, 0, 0};
-  mt_acc[0] = mt_acc[1] = -__builtin_inff();
+  rs[1][0] = rs[1][1] = 0.f;
   const f32x16 zero = {};
   float fa[8], fb[8];  // staged pair values
 
@@ -372,6 +378,7 @@ void attn_kernel(AttnParams p) {
     for (int k = 0; k < 8; ++k) {
       const int fs = k * N / 8;
       const int n = lo + k, b = n >> 3, e = 2 * (n & 7);
+      if (fs + 3 == i) rs[qb][k & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[qb][n], kOnes2, rs[qb][k & 1], false);
       if (fs + 2 == i) pw[qb][n] = cvt_bf16x2(fa[k], fb[k]);
       if (fs + 1 == i) {
         fa[k] = fast_exp2(fa[k]);
@@ -379,28 +386,23 @@ void attn_kernel(AttnParams p) {
       }
       if (fs == i) {
         const float x0 = sa[b][e], x1 = sa[b][e + 1];
-        mt_acc[qb] = __builtin_fmaxf(mt_acc[qb], __builtin_fmaxf(x0, x1));
         fa[k] = __builtin_fmaf(x0, c2, -mc[qb]);
         fb[k] = __builtin_fmaf(x1, c2, -mc[qb]);
       }
     }
   };
-  auto rows_at = [&](int qb, int steps, int i) __attribute__((always_inline)) {
-#pragma unroll
-    for (int k = i * 16 / steps; k < (i + 1) * 16 / steps; ++k)
-      rs[qb][k & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[qb][k], kOnes2, rs[qb][k & 1], false);
-  };
-  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid) __attribute__((always_inline)) {
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, bool first) __attribute__((always_inline)) {
     pin_p(qb);
-    asm volatile("" ::"v"(mt_acc[qb]));
-    if (valid < kBN || __builtin_amdgcn_ballot_w64(pair_max(mt_acc[qb]) > m_run[qb] + lazy_raw) != 0)
+    asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
+    if (first || valid < kBN || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
       slow_block(qb, sa, valid);
+    l_run[qb] += rs[qb][0] + rs[qb][1];
     __builtin_amdgcn_sched_barrier(0);
   };
-  // PV slot of block qb: N matrix ops (when `mma`), then two tail steps for the staged pairs.
+  // PV slot of block qb: N matrix ops (when `mma`), then three tail steps for the staged pairs.
   auto pv_slot = [&](int qb, bool mma, auto&& extra) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NP + 2; ++i) {
+    for (int i = 0; i < NP + 3; ++i) {
       if (mma && i < NP) {
         const int b = i / (2 * DB), tt = (i / DB) & 1, db = i % DB;
         oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(b, tt, db), pfrag(qb, b, tt), oacc[qb][db], 0, 0, 0);
@@ -411,7 +413,7 @@ void attn_kernel(AttnParams p) {
   };
   auto s_slot = [&](int qb, f32x16 (&sa)[2], bool mma, auto&& extra) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NS + 2; ++i) {
+    for (int i = 0; i < NS + 3; ++i) {
       if (mma && i < NS) {
         const int st = i >> 1, b = i & 1;
         sa[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st][b], qf[qb][st], st == 0 ? zero : sa[b], 0, 0, 0);
@@ -472,23 +474,19 @@ void attn_kernel(AttnParams p) {
         stage_at(1, s1, 8, NS, i);
         if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)));
       });
-      check_block(1, s1, valid_prev);
+      check_block(1, s1, valid_prev, t == 1);
       // slot 1
-      rs[1][0] = rs[1][1] = 0.f;
-      mt_acc[0] = -__builtin_inff();
+      rs[0][0] = rs[0][1] = 0.f;
       pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
         if (i < NP) {
           read_v(vb, 2 * i);
           read_v(vb, 2 * i + 1);
         }
         stage_at(0, s0, 0, NP, i);
-        if (i < NP) rows_at(1, NP, i);
       });
-      asm volatile("" ::"v"(rs[1][0]), "v"(rs[1][1]));
-      l_run[1] += rs[1][0] + rs[1][1];
       // slot 2
       s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
-      check_block(0, s0, valid);
+      check_block(0, s0, valid, t == 0);
     } else {
 #pragma unroll
       for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx);
@@ -499,19 +497,15 @@ void attn_kernel(AttnParams p) {
 
     if (wave_active) {
       // slot 3 (after the last tile the K reads hit a buffer nobody uses)
-      rs[0][0] = rs[0][1] = 0.f;
-      mt_acc[1] = -__builtin_inff();
+      rs[1][0] = rs[1][1] = 0.f;
       pv_slot(0, true, [&](int i) __attribute__((always_inline)) {
         if (i < NP) {
 #pragma unroll
           for (int r = 0; r < 2 * KS / NP; ++r) read_k(kb_next, i * (2 * KS / NP) + r);
-          rows_at(0, NP, i);
           if (i % (NP / (NLD / 2)) == 0) dma_load(t + 3, i / (NP / (NLD / 2)));
         }
         stage_at(1, s1, 0, NP, i);
       });
-      asm volatile("" ::"v"(rs[0][0]), "v"(rs[0][1]));
-      l_run[0] += rs[0][0] + rs[0][1];
     } else {
 #pragma unroll
       for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx);
@@ -521,12 +515,8 @@ void attn_kernel(AttnParams p) {
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no DMA may still write this block's LDS at exit
   if (wave_active) {  // block 1 of the last tile
     s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { stage_at(1, s1, 8, NS, i); });
-    check_block(1, s1, valid_prev);
-    rs[1][0] = rs[1][1] = 0.f;
-    pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
-      if (i < NP) rows_at(1, NP, i);
-    });
-    l_run[1] += rs[1][0] + rs[1][1];
+    check_block(1, s1, valid_prev, nt == 1);
+    pv_slot(1, true, [&](int) __attribute__((always_inline)) {});
   }
 #undef WA_WAIT_VMCNT
 
