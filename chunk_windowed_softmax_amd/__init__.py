@@ -8,7 +8,8 @@ Functions carry the C names:
 
 * ``wa_plan_create(T, S, G, K, radius, H, d) -> Plan``
 * ``wa_forward(plan, q, k, v, out=None) -> out``
-* ``wa_plan_info / wa_plan_groups / wa_plan_kv_indices / wa_plan_items / wa_last_error``
+* ``wa_plan_info / wa_plan_groups / wa_plan_kv_indices / wa_plan_items / wa_plan_launch_order /
+  wa_last_error``
 """
 
 from __future__ import annotations
@@ -35,6 +36,7 @@ EXPORTED_SYMBOLS = (
     "wa_plan_groups",
     "wa_plan_kv_indices",
     "wa_plan_items",
+    "wa_plan_launch_order",
     "wa_last_error",
 )
 
@@ -52,6 +54,7 @@ class _PlanInfo(ctypes.Structure):
         ("n_chunks", ctypes.c_int32), ("n_groups", ctypes.c_int32), ("kept_pairs_per_head", ctypes.c_int64),
         ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("n_splits", ctypes.c_int32),
         ("n_items", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
+        ("launch_xcds", ctypes.c_int32), ("launch_per_xcd", ctypes.c_int32),
     ]
 
 
@@ -79,6 +82,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wa_plan_groups.argtypes = [P, i32p, ctypes.c_size_t]
     lib.wa_plan_kv_indices.argtypes = [P, ctypes.c_int, i32p, ctypes.c_size_t]
     lib.wa_plan_items.argtypes = [P, i32p, ctypes.c_size_t]
+    lib.wa_plan_launch_order.argtypes = [P, i32p, ctypes.c_size_t]
     lib.wa_last_error.argtypes = []
     lib.wa_last_error.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS:
@@ -163,6 +167,15 @@ def wa_plan_items(plan: Plan) -> np.ndarray:
     return arr[:n].reshape(-1, WA_ITEM_COLS)
 
 
+def wa_plan_launch_order(plan: Plan) -> np.ndarray:
+    """[launch_xcds, launch_per_xcd] int32: the work unit (head * n_items + item) of each
+    block's slot, -1 for none."""
+    x, per = plan.info["launch_xcds"], plan.info["launch_per_xcd"]
+    arr, ptr = _int32_buffer(x * per)
+    _check(load_library().wa_plan_launch_order(plan.handle, ptr, arr.size))
+    return arr[: x * per].reshape(x, per)
+
+
 def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
     """Run the decomposed window attention; returns ``out`` ([L, H, d], dtype of q).
 
@@ -201,4 +214,5 @@ def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
 __all__ = [
     "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
     "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
+    "wa_plan_launch_order",
 ]

@@ -79,10 +79,14 @@ int device_resources(wa_plan* p, DeviceResources** out) {
     return WA_OK;
   }
   DeviceResources r;
+  // items, then the launch order (int32), in one allocation
   const size_t item_bytes = p->host.items.size() * sizeof(wa::Item);
-  e = hipMalloc(&r.items, item_bytes);
+  const size_t work_bytes = p->host.work.size() * sizeof(int32_t);
+  e = hipMalloc(&r.items, item_bytes + work_bytes);
   if (e != hipSuccess) return fail(WA_ERR_ALLOC, std::string("hipMalloc(items): ") + hipGetErrorString(e));
   e = hipMemcpy(r.items, p->host.items.data(), item_bytes, hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(reinterpret_cast<char*>(r.items) + item_bytes, p->host.work.data(), work_bytes, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(r.items);
     return fail(WA_ERR_HIP, std::string("hipMemcpy(items): ") + hipGetErrorString(e));
@@ -186,6 +190,8 @@ int wa_plan_info(const wa_plan* plan, wa_plan_info_t* info) {
   info->block_n = h.block_n;
   info->n_splits = h.n_splits;
   info->n_items = (int32_t)h.items.size();
+  info->launch_xcds = wa::kXcdCount;
+  info->launch_per_xcd = h.work_per_xcd;
   info->workspace_bytes = h.partial_bytes;
   return WA_OK;
 }
@@ -223,6 +229,14 @@ int wa_plan_items(const wa_plan* plan, int32_t* dst, size_t n) {
   const auto& items = plan->host.items;
   if (n < items.size() * WA_ITEM_COLS) return fail(WA_ERR_INVALID, "wa_plan_items: destination too small");
   std::memcpy(dst, items.data(), items.size() * sizeof(wa::Item));
+  return WA_OK;
+}
+
+int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n) {
+  if (!plan || !dst) return fail(WA_ERR_INVALID, "wa_plan_launch_order: NULL argument");
+  const auto& work = plan->host.work;
+  if (n < work.size()) return fail(WA_ERR_INVALID, "wa_plan_launch_order: destination too small");
+  std::memcpy(dst, work.data(), work.size() * sizeof(int32_t));
   return WA_OK;
 }
 
@@ -285,6 +299,8 @@ int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v
   a.block_m = h.block_m;
   a.items = r->items;
   a.n_items = (int)h.items.size();
+  a.work = reinterpret_cast<const int32_t*>(r->items + h.items.size());
+  a.work_per_xcd = h.work_per_xcd;
   a.n_splits = h.n_splits;
   a.part_o = r->part;
   a.part_ml = r->part ? r->part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;

@@ -38,8 +38,10 @@
 //   and a wave-uniform slow path raises it (rescaling the accumulators) only when some
 //   row's max grew by more than 2^8 (values up to 2^8 are exact in the softmax ratio);
 //   the same path masks keys past a segment end.
-//   Blocks are remapped so that consecutive work items (same head, same group, adjacent
-//   query tiles sharing all their keys) land on the same XCD and share its L2.
+//   Blocks take their work unit from the plan's launch-order table: each XCD (blocks are
+//   dispatched round-robin over the XCDs) gets a contiguous run of window units, so the
+//   query tiles of one group run side by side and share that XCD's L2, followed by its
+//   share of the shorter global-leg units, which even out the end of the launch.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -63,7 +65,7 @@ constexpr int kWaveRows = 64;  // query rows per wave (two 32-row blocks)
 constexpr int kBN = kBlockN;   // keys per tile
 static_assert(kBN == 64, "the fragment code below assumes 64-key tiles");
 
-constexpr int kXcds = 8;  // MI355X: blocks are dispatched round-robin over 8 XCDs
+constexpr int kXcds = kXcdCount;  // blocks are dispatched round-robin over the XCDs
 
 // 16-byte chunk swizzle of an LDS row.  The LDS has 64 banks (256 bytes per pass); a
 // ds_read_b128 pass serves 16 lanes and a ds_read_tr16_b64 pass 32 lanes.
@@ -103,6 +105,7 @@ struct AttnParams {
   const uint16_t* __restrict__ v;
   void* __restrict__ out;
   const Item* __restrict__ items;
+  const int32_t* __restrict__ work;
   float* __restrict__ part_o;
   float* __restrict__ part_ml;
   int H, G, frame_rows, n_items, total, per_xcd;
@@ -146,10 +149,10 @@ void attn_kernel(AttnParams p) {
   const int l32 = lane & 31;
 
   const int bid = blockIdx.x;
-  const int logical = (bid % kXcds) * p.per_xcd + bid / kXcds;
-  if (logical >= p.total) return;
-  const int h = logical / p.n_items;
-  const Item it = p.items[logical - h * p.n_items];
+  const int unit = p.work[(bid % kXcds) * p.per_xcd + bid / kXcds];
+  if (unit < 0) return;
+  const int h = unit / p.n_items;
+  const Item it = p.items[unit - h * p.n_items];
   const int H = p.H;
   const uint32_t row_bytes = uint32_t(H) * D * 2;  // bytes between consecutive rows of q/k/v
 
@@ -250,16 +253,19 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
     for (int n = 0; n < 16; ++n) pw[qb][n] = cvt_bf16x2(0.f, 0.f);
 
-  auto read_k = [&](const unsigned char* kb, int idx) __attribute__((always_inline)) {
+  // koff / voff hold the byte offset of the ring slot being read (K: the tile after the
+  // current one; V: the current tile) plus the lane's part; they advance once per tile.
+  auto read_k = [&](int idx) __attribute__((always_inline)) {
     const int s = idx >> 1, b = idx & 1;
-    kf[s][b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kb + koff[s] + b * 32 * ROWB));
+    kf[s][b] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(smem + koff[s] + b * 32 * ROWB));
   };
-  auto read_v = [&](const unsigned char* vb, int idx) __attribute__((always_inline)) {
+  auto read_v = [&](int idx) __attribute__((always_inline)) {
     const int f = idx >> 1, rr = idx & 1;
     const int b = f / (2 * DB), tt = (f / DB) & 1, db = f % DB;
-    const unsigned char* vt = vb + (32 * b + 16 * tt) * ROWB;
-    vr[f][rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vt + voff[db][rr]));
+    vr[f][rr] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(smem + voff[db][rr] + (32 * b + 16 * tt) * ROWB));
   };
+  // byte offset of ring slot r's K (V: + TILEB)
+  auto ring = [](int r) __attribute__((always_inline)) -> uint32_t { return uint32_t(r % NBUF) * 2 * TILEB; };
   auto vfrag = [&](int b, int tt, int db) __attribute__((always_inline)) -> bf16x8 {
     const int f = (b * 2 + tt) * DB + db;
     const u32x4 vw = {__builtin_bit_cast(u32x2, vr[f][0])[0], __builtin_bit_cast(u32x2, vr[f][0])[1],
@@ -457,13 +463,17 @@ void attn_kernel(AttnParams p) {
   barrier();
   if (wave_active) {
 #pragma unroll
-    for (int i = 0; i < 2 * KS; ++i) read_k(smem, i);
+    for (int i = 0; i < 2 * KS; ++i) read_k(i);
   }
+#pragma unroll
+  for (int st = 0; st < KS; ++st) koff[st] += ring(1);  // from here on: the tile after the current
+#pragma unroll
+  for (int db = 0; db < DB; ++db) voff[db][0] += TILEB, voff[db][1] += TILEB;
 
   int valid_prev = kBN;
   for (int t = 0; t < nt; ++t) {
-    const unsigned char* vb = smem + (2 * (t % NBUF) + 1) * TILEB;
-    const unsigned char* kb_next = smem + (2 * ((t + 1) % NBUF)) * TILEB;
+    const uint32_t step_k = ring(t + 2) - ring(t + 1);  // slot advance after this tile's reads
+    const uint32_t step_v = ring(t + 1) - ring(t);
     int n0, nend;
     tile_range(t, n0, nend);
     const int valid = nend - n0;
@@ -479,11 +489,13 @@ void attn_kernel(AttnParams p) {
       rs[0][0] = rs[0][1] = 0.f;
       pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
         if (i < NP) {
-          read_v(vb, 2 * i);
-          read_v(vb, 2 * i + 1);
+          read_v(2 * i);
+          read_v(2 * i + 1);
         }
         stage_at(0, s0, 0, NP, i);
       });
+#pragma unroll
+      for (int db = 0; db < DB; ++db) voff[db][0] += step_v, voff[db][1] += step_v;
       // slot 2
       s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
       check_block(0, s0, valid, t == 0);
@@ -501,11 +513,13 @@ void attn_kernel(AttnParams p) {
       pv_slot(0, true, [&](int i) __attribute__((always_inline)) {
         if (i < NP) {
 #pragma unroll
-          for (int r = 0; r < 2 * KS / NP; ++r) read_k(kb_next, i * (2 * KS / NP) + r);
+          for (int r = 0; r < 2 * KS / NP; ++r) read_k(i * (2 * KS / NP) + r);
           if (i % (NP / (NLD / 2)) == 0) dma_load(t + 3, i / (NP / (NLD / 2)));
         }
         stage_at(1, s1, 0, NP, i);
       });
+#pragma unroll
+      for (int st = 0; st < KS; ++st) koff[st] += step_k;
     } else {
 #pragma unroll
       for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx);
@@ -632,8 +646,9 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   p.G = a.G;
   p.frame_rows = a.frame_rows;
   p.n_items = a.n_items;
-  p.total = a.n_items * a.H;
-  p.per_xcd = (p.total + kXcds - 1) / kXcds;
+  p.work = a.work;
+  p.per_xcd = a.work_per_xcd;
+  p.total = kXcds * a.work_per_xcd;
   p.scale_log2 = a.scale_log2;
   const int grid = p.per_xcd * kXcds;
   hipLaunchKernelGGL((attn_kernel<D, OUT_F32>), dim3(grid), dim3(kNW * 64), 0, stream, p);

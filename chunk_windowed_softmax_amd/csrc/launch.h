@@ -19,6 +19,8 @@ struct ForwardArgs {
   int block_m;            // query rows per work item: 256 (4 waves x 64 rows)
   const Item* items;      // device copy of the plan's items
   int n_items;
+  const int32_t* work;    // device copy of the launch order (kXcdCount * work_per_xcd units)
+  int work_per_xcd;
   int n_splits;           // > 1: global-leg items write partials, then a combine pass
   float* part_o;          // [n_splits, G, H, d] fp32
   float* part_ml;         // [n_splits, G, H, 2] fp32: running max (log2 units), row sum

@@ -85,11 +85,13 @@ int build_plan(const Geometry& g, HostPlan* out, std::string* err) {
   }
   p.n_window_items = int32_t(p.items.size());
 
-  // Second leg: the G global rows over all L keys.  The keys are split so that one split
-  // is about as long as the longest window item; splits are whole key tiles.
+  // Second leg: the G global rows over all L keys, split into whole key tiles (split length
+  // as set out next to kGlobalSplitDiv).
   p.n_splits = 0;
   if (g.G > 0) {
-    int64_t n_splits = std::max<int64_t>(1, (p.L + max_window_kv - 1) / max_window_kv);
+    const bool fine = int64_t(p.n_window_items) * g.H >= int64_t(kFineSplitRounds) * kComputeUnits;
+    const int64_t split_len = std::max<int64_t>(p.block_n, max_window_kv / (fine ? kGlobalSplitDiv : 1));
+    int64_t n_splits = std::max<int64_t>(1, (p.L + split_len - 1) / split_len);
     int64_t chunk = (p.L + n_splits - 1) / n_splits;
     chunk = (chunk + p.block_n - 1) / p.block_n * p.block_n;
     n_splits = (p.L + chunk - 1) / chunk;
@@ -109,6 +111,21 @@ int build_plan(const Geometry& g, HostPlan* out, std::string* err) {
     }
     if (p.n_splits > 1)
       p.partial_bytes = int64_t(p.n_splits) * g.G * g.H * (g.d + 2) * int64_t(sizeof(float));
+  }
+
+  // Launch order (see HostPlan::work).
+  const int32_t n_items = int32_t(p.items.size());
+  std::vector<int32_t> win, glob;
+  for (int32_t h = 0; h < g.H; ++h)
+    for (int32_t i = 0; i < n_items; ++i) (i < p.n_window_items ? win : glob).push_back(h * n_items + i);
+  const int32_t pw = int32_t((win.size() + kXcdCount - 1) / kXcdCount);
+  const int32_t pg = int32_t((glob.size() + kXcdCount - 1) / kXcdCount);
+  p.work_per_xcd = pw + pg;
+  p.work.assign(size_t(kXcdCount) * p.work_per_xcd, -1);
+  for (int x = 0; x < kXcdCount; ++x) {
+    int32_t* dst = p.work.data() + size_t(x) * p.work_per_xcd;
+    for (int32_t j = 0; j < pw && size_t(x) * pw + j < win.size(); ++j) dst[j] = win[size_t(x) * pw + j];
+    for (int32_t j = 0; j < pg && size_t(x) * pg + j < glob.size(); ++j) dst[pw + j] = glob[size_t(x) * pg + j];
   }
   *out = std::move(p);
   return 0;

@@ -42,10 +42,24 @@ struct HostPlan {
   std::vector<Group> groups;
   std::vector<Item> items;  // window items (group-major), then global-leg items (split-major)
   int64_t partial_bytes = 0;  // device workspace of the global leg's partial results
+  // Launch order: entry b of XCD x (block x + 8 b) is unit work[x * work_per_xcd + b], unit =
+  // head * items.size() + item, or -1 (no work).  Each XCD gets a contiguous run of window
+  // units (same group's query tiles side by side, sharing its L2) and then a run of the
+  // shorter global-leg units, so the last blocks to start are the short ones.
+  std::vector<int32_t> work;
+  int32_t work_per_xcd = 0;
 };
 
 constexpr int kBlockM = 256;  // query rows per work item: 4 waves x 64 rows
 constexpr int kBlockN = 64;   // keys per staged K/V tile
+constexpr int kXcdCount = 8;  // MI355X: workgroups are dispatched round-robin over 8 XCDs
+// When the window leg alone fills the chip for several rounds, a global-leg key split is
+// about 1/kGlobalSplitDiv of the longest window item: the short units finish each XCD's
+// queue and even out the tail of the launch.  Otherwise one split is about as long as the
+// longest window item (fewer partial results to merge).
+constexpr int kGlobalSplitDiv = 3;
+constexpr int kComputeUnits = 256;   // MI355X
+constexpr int kFineSplitRounds = 4;  // window units >= this many rounds of all compute units
 
 // Status codes mirror the C ABI (0 ok, 1 invalid, 2 unsupported).
 int build_plan(const Geometry& g, HostPlan* out, std::string* err);

@@ -64,6 +64,8 @@ typedef struct wa_plan_info_t {
   int32_t n_splits;                 /* key splits of the global leg (1 = no split) */
   int32_t n_items;                  /* work items per head (both legs) */
   int64_t workspace_bytes;          /* device workspace of the global leg's partials */
+  int32_t launch_xcds;              /* launch order: number of XCD queues ... */
+  int32_t launch_per_xcd;           /* ... and entries per queue (see wa_plan_launch_order) */
 } wa_plan_info_t;
 
 /* Columns of one row of wa_plan_items(). */
@@ -147,6 +149,16 @@ int wa_plan_kv_indices(const wa_plan* plan, int g, int32_t* dst, size_t n);
  * WA_ERR_INVALID if n is too small.
  */
 int wa_plan_items(const wa_plan* plan, int32_t* dst, size_t n);
+
+/*
+ * wa_plan_launch_order -- copy the launch order to host memory: launch_xcds * launch_per_xcd
+ * int32 entries; entry j of queue x is the work unit that block (x + launch_xcds * j) runs,
+ * unit = head * n_items + item, or -1 for a block with no work.  Each unit appears exactly
+ * once.  (The attention launch takes blocks round-robin over the XCDs; each queue holds a
+ * contiguous run of window units and then the shorter global-leg units.)
+ * WA_ERR_INVALID if n is too small.
+ */
+int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n);
 
 /* wa_last_error -- message of the calling thread's last non-zero status ("" if none). */
 const char* wa_last_error(void);

@@ -52,7 +52,28 @@ def _check_plan_against_oracle(T, S, G, K, r, H, d):
     assert info["kept_pairs_per_head"] == kept_pairs_per_head(geom)
     assert info["L"] == geom.L and info["n_chunks"] == geom.n_chunks and info["n_groups"] == len(ref)
     _check_items_cover(plan, geom)
+    _check_launch_order(plan, H)
     return plan
+
+
+def _check_launch_order(plan, H):
+    """The launch order runs every (head, item) unit exactly once; per XCD queue the window
+    units come first, in increasing order (a contiguous run), then the global-leg units."""
+    info = plan.info
+    order = wa.wa_plan_launch_order(plan)
+    assert order.shape == (info["launch_xcds"], info["launch_per_xcd"])
+    n_items = info["n_items"]
+    items = wa.wa_plan_items(plan)
+    n_window = int((items[:, 0] < info["T"] * info["S"]).sum())
+    units = order[order >= 0]
+    assert sorted(units.tolist()) == list(range(H * n_items))
+    for queue in order:
+        q = queue[queue >= 0]
+        is_win = (q % n_items) < n_window
+        k = int(is_win.sum())
+        assert is_win[:k].all() and not is_win[k:].any()
+        if k:
+            assert (np.diff(q[:k]) > 0).all()
 
 
 def _check_items_cover(plan, geom):
@@ -130,6 +151,8 @@ def test_null_arguments(lib):
     assert lib.wa_plan_groups(plan.handle, small, 1) == wa.WA_ERR_INVALID
     assert lib.wa_plan_kv_indices(plan.handle, 99, small, 1) == wa.WA_ERR_INVALID
     assert lib.wa_plan_items(plan.handle, small, 1) == wa.WA_ERR_INVALID
+    assert lib.wa_plan_launch_order(plan.handle, small, 0) == wa.WA_ERR_INVALID
+    assert lib.wa_plan_launch_order(None, small, 1) == wa.WA_ERR_INVALID
 
 
 def test_plan_cache_and_refcounts(lib):
