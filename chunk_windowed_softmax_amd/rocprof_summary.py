@@ -124,6 +124,7 @@ def main() -> int:
         "kernel": ATTN,
         "kernel_source_sha256": kernel_source_sha256(),
         "avg_duration_ms": attn_ns / 1e6,
+        "median_duration_ms": statistics.median(dur[ATTN]) / 1e6,
         "calls": len(dur[ATTN]),
         "tflops_at_avg_duration": a.flop_per_call / (attn_ns * 1e-9) / 1e12,
         "fetch_kib_raw": fetch[ATTN],
@@ -170,11 +171,12 @@ def main() -> int:
         f"- FETCH_SIZE:   `{a.command_fetch}`",
         f"- WRITE_SIZE:   `{a.command_write}`",
         "",
-        "| kernel | calls | avg ms | min ms | max ms |",
-        "|---|---|---|---|---|",
+        "| kernel | calls | avg ms | median ms | min ms | max ms |",
+        "|---|---|---|---|---|---|",
     ]
     for k, v in sorted(dur.items()):
-        lines.append(f"| {k} | {len(v)} | {statistics.fmean(v)/1e6:.4f} | {min(v)/1e6:.4f} | {max(v)/1e6:.4f} |")
+        lines.append(f"| {k} | {len(v)} | {statistics.fmean(v)/1e6:.4f} | {statistics.median(v)/1e6:.4f} | "
+                     f"{min(v)/1e6:.4f} | {max(v)/1e6:.4f} |")
     lines += [
         "",
         f"Kept-pair FLOP per call: {a.flop_per_call:.6g}; at the average `{ATTN}` duration: "
