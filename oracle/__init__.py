@@ -18,3 +18,9 @@ from .window_attention import (  # noqa: F401
     window_bounds,
     window_mask,
 )
+from .causal_attention import (  # noqa: F401
+    causal_attention_reference,
+    causal_attention_rows,
+    causal_mask,
+    causal_pairs_per_head,
+)
