@@ -28,7 +28,8 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="h3", help="workload name (h3, h3_full, small, ragged, dense)")
+    ap.add_argument("--workload", default="h3",
+                    help="workload name (h3, h3_full, small, ragged, dense, audio_causal, audio_causal_small)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads of the workload the CPU oracle runs")
     ap.add_argument("--calibration-copy", action="store_true",
@@ -52,20 +53,26 @@ def cpu_baseline(w, q, k, v, heads: int) -> dict:
     """Time the fp64 oracle (as it stands) on the first `heads` heads of the workload."""
     import numpy as np  # noqa: F401
 
-    from oracle import Geometry, kept_pairs_per_head, window_attention_reference
+    from oracle import (Geometry, causal_attention_reference, causal_pairs_per_head, kept_pairs_per_head,
+                        window_attention_reference)
 
-    geom = Geometry(*w.geometry)
     qs, ks, vs = (x[:, :heads].contiguous() for x in (q, k, v))
     t0 = time.perf_counter()
-    window_attention_reference(qs, ks, vs, geom)
+    if w.causal:
+        causal_attention_reference(qs, ks, vs)
+        pairs = causal_pairs_per_head(w.L)
+    else:
+        geom = Geometry(*w.geometry)
+        window_attention_reference(qs, ks, vs, geom)
+        pairs = kept_pairs_per_head(geom)
     dt = time.perf_counter() - t0
-    flop = kept_pairs_per_head(geom) * heads * 4 * w.d
+    flop = pairs * heads * 4 * w.d
     return {
         "value": round(flop / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": _cpu_threads(),
         "kind": "oracle",
-        "sample": f"fp64 numpy per-frame oracle on {heads} of {w.H} heads of the {w.name} workload "
+        "sample": f"fp64 numpy {'causal' if w.causal else 'per-frame'} oracle on {heads} of {w.H} heads of the {w.name} workload "
                   f"(all {w.L} rows), {dt:.1f} s wall",
         "seconds": round(dt, 3),
     }
@@ -109,7 +116,10 @@ def main() -> int:
     out = torch.empty_like(q)
 
     t0 = time.perf_counter()
-    plan = wa.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
+    if w.causal:
+        plan = wa.wa_causal_plan_create(w.L, w.H, w.d)
+    else:
+        plan = wa.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
     plan_ms = (time.perf_counter() - t0) * 1e3
     info = plan.info
     flop = info["kept_pairs_per_head"] * w.H * 4 * w.d

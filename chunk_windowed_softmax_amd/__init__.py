@@ -7,6 +7,7 @@ stream.  There is no fallback: if the library is missing the calls raise.
 Functions carry the C names:
 
 * ``wa_plan_create(T, S, G, K, radius, H, d) -> Plan``
+* ``wa_causal_plan_create(n, H, d) -> Plan`` (causal dense attention, the audio VAE's)
 * ``wa_forward(plan, q, k, v, out=None) -> out``
 * ``wa_plan_info / wa_plan_groups / wa_plan_kv_indices / wa_plan_items / wa_plan_launch_order /
   wa_last_error``
@@ -30,6 +31,7 @@ WA_ITEM_COLS = 8
 # Every symbol include/wa.h declares.
 EXPORTED_SYMBOLS = (
     "wa_plan_create",
+    "wa_causal_plan_create",
     "wa_plan_release",
     "wa_forward",
     "wa_plan_info",
@@ -54,7 +56,7 @@ class _PlanInfo(ctypes.Structure):
         ("n_chunks", ctypes.c_int32), ("n_groups", ctypes.c_int32), ("kept_pairs_per_head", ctypes.c_int64),
         ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("n_splits", ctypes.c_int32),
         ("n_items", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
-        ("launch_xcds", ctypes.c_int32), ("launch_per_xcd", ctypes.c_int32),
+        ("launch_xcds", ctypes.c_int32), ("launch_per_xcd", ctypes.c_int32), ("causal", ctypes.c_int32),
     ]
 
 
@@ -76,6 +78,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     P = ctypes.c_void_p
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.wa_plan_create.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(P)]
+    lib.wa_causal_plan_create.argtypes = [ctypes.c_int] * 3 + [ctypes.POINTER(P)]
     lib.wa_plan_release.argtypes = [P]
     lib.wa_forward.argtypes = [P, P, P, P, P, ctypes.c_int, P]
     lib.wa_plan_info.argtypes = [P, ctypes.POINTER(_PlanInfo)]
@@ -128,6 +131,14 @@ def wa_plan_create(T: int, S: int, G: int, K: int, radius: int, H: int, d: int) 
     lib = load_library()
     h = ctypes.c_void_p()
     _check(lib.wa_plan_create(T, S, G, K, radius, H, d, ctypes.byref(h)))
+    return Plan(h)
+
+
+def wa_causal_plan_create(n: int, H: int, d: int) -> Plan:
+    """Plan for causal dense attention over n rows ([n, H, d] tensors; row i sees keys 0..i)."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.wa_causal_plan_create(n, H, d, ctypes.byref(h)))
     return Plan(h)
 
 
@@ -214,5 +225,5 @@ def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
 __all__ = [
     "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
     "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
-    "wa_plan_launch_order",
+    "wa_plan_launch_order", "wa_causal_plan_create",
 ]

@@ -113,10 +113,10 @@ bool overlaps(const void* a, const void* b, size_t n) {
 
 extern "C" {
 
-int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan** out) {
-  if (!out) return fail(WA_ERR_INVALID, "wa_plan_create: out is NULL");
+// Fetch the cached plan of `geo` or build and cache it (shared by both plan constructors).
+static int create_cached(const wa::Geometry& geo, wa_plan** out, const char* who) {
+  if (!out) return fail(WA_ERR_INVALID, std::string(who) + ": out is NULL");
   *out = nullptr;
-  const wa::Geometry geo{T, S, G, K, radius, H, d};
   {
     std::lock_guard<std::mutex> lk(g_cache_mu);
     for (auto it = g_cache.begin(); it != g_cache.end(); ++it) {
@@ -132,13 +132,13 @@ int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan
   }
   wa::HostPlan hp;
   std::string err;
-  const int st = wa::build_plan(geo, &hp, &err);
-  if (st != 0) return fail(st, "wa_plan_create: " + err);
+  const int st = geo.causal ? wa::build_causal_plan(geo.S, geo.H, geo.d, &hp, &err) : wa::build_plan(geo, &hp, &err);
+  if (st != 0) return fail(st, std::string(who) + ": " + err);
   wa_plan* p = nullptr;
   try {
     p = new wa_plan();
   } catch (...) {
-    return fail(WA_ERR_ALLOC, "wa_plan_create: out of host memory");
+    return fail(WA_ERR_ALLOC, std::string(who) + ": out of host memory");
   }
   p->host = std::move(hp);
   p->refs.store(2);  // the caller's handle + the cache's
@@ -163,6 +163,14 @@ int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan
   if (evicted) unref(evicted);
   *out = p;
   return WA_OK;
+}
+
+int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan** out) {
+  return create_cached(wa::Geometry{T, S, G, K, radius, H, d, 0}, out, "wa_plan_create");
+}
+
+int wa_causal_plan_create(int n, int H, int d, wa_plan** out) {
+  return create_cached(wa::Geometry{1, n, 0, 1, 0, H, d, 1}, out, "wa_causal_plan_create");
 }
 
 int wa_plan_release(wa_plan* plan) {
@@ -190,6 +198,7 @@ int wa_plan_info(const wa_plan* plan, wa_plan_info_t* info) {
   info->block_n = h.block_n;
   info->n_splits = h.n_splits;
   info->n_items = (int32_t)h.items.size();
+  info->causal = h.geo.causal;
   info->launch_xcds = wa::kXcdCount;
   info->launch_per_xcd = h.work_per_xcd;
   info->workspace_bytes = h.partial_bytes;

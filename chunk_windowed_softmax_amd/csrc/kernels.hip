@@ -159,6 +159,7 @@ void attn_kernel(AttnParams p) {
   // ---- Q fragments (B operand of S^T = K Q^T): lane = query row, 8 d each
   const int row0 = it.q_begin + wave * kWaveRows;
   const bool wave_active = row0 < it.q_end;
+  const bool causal = (it.flags & kItemCausal) != 0;  // row r sees keys <= r only
   bf16x8 qf[2][KS];  // loaded in the prologue below, together with the first K/V tile
 
   // ---- DMA source offsets: LDS slice j holds tile rows [j*1024/ROWB, ...); lane writes LDS
@@ -308,9 +309,13 @@ void attn_kernel(AttnParams p) {
   // Slow path of one query block (wave-uniform): mask keys past the segment end, raise the
   // running max (rescaling the accumulators) when it grew by more than 2^8, redo P and its
   // row sums.
-  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid) __attribute__((always_inline)) {
-    if (valid < kBN) {
-      const int lim = valid - 4 * hh;  // key (b*32 + (i/4)*8 + 4*hh + i%4) >= valid
+  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0) __attribute__((always_inline)) {
+    if (valid < kBN || causal) {
+      // tile keys at or past `lim` are masked: the segment end, and for causal items also
+      // every key after this lane's own query row
+      int lim = valid;
+      if (causal) lim = __builtin_elementwise_min(lim, row0 + 32 * qb + l32 - n0 + 1);
+      lim -= 4 * hh;  // key (b*32 + (i/4)*8 + 4*hh + i%4) >= valid
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -397,11 +402,12 @@ void attn_kernel(AttnParams p) {
       }
     }
   };
-  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, bool first) __attribute__((always_inline)) {
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool first) __attribute__((always_inline)) {
     pin_p(qb);
     asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
-    if (first || valid < kBN || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
-      slow_block(qb, sa, valid);
+    if (first || valid < kBN || (causal && n0 + kBN - 1 > row0 + 32 * qb) ||
+        __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
+      slow_block(qb, sa, valid, n0);
     l_run[qb] += rs[qb][0] + rs[qb][1];
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -470,7 +476,7 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) voff[db][0] += TILEB, voff[db][1] += TILEB;
 
-  int valid_prev = kBN;
+  int valid_prev = kBN, n0_prev = 0;
   for (int t = 0; t < nt; ++t) {
     const uint32_t step_k = ring(t + 2) - ring(t + 1);  // slot advance after this tile's reads
     const uint32_t step_v = ring(t + 1) - ring(t);
@@ -484,7 +490,7 @@ void attn_kernel(AttnParams p) {
         stage_at(1, s1, 8, NS, i);
         if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)));
       });
-      check_block(1, s1, valid_prev, t == 1);
+      check_block(1, s1, valid_prev, n0_prev, t == 1);
       // slot 1
       rs[0][0] = rs[0][1] = 0.f;
       pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
@@ -498,7 +504,7 @@ void attn_kernel(AttnParams p) {
       for (int db = 0; db < DB; ++db) voff[db][0] += step_v, voff[db][1] += step_v;
       // slot 2
       s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
-      check_block(0, s0, valid, t == 0);
+      check_block(0, s0, valid, n0, t == 0);
     } else {
 #pragma unroll
       for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx);
@@ -525,11 +531,12 @@ void attn_kernel(AttnParams p) {
       for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx);
     }
     valid_prev = valid;
+    n0_prev = n0;
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no DMA may still write this block's LDS at exit
   if (wave_active) {  // block 1 of the last tile
     s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { stage_at(1, s1, 8, NS, i); });
-    check_block(1, s1, valid_prev, nt == 1);
+    check_block(1, s1, valid_prev, n0_prev, nt == 1);
     pv_slot(1, true, [&](int) __attribute__((always_inline)) {});
   }
 #undef WA_WAIT_VMCNT

@@ -5,6 +5,8 @@
 
 namespace wa {
 
+void build_launch_order(HostPlan* p);
+
 namespace {
 
 // Rows [begin, end) of the whole chunks lo..hi; the last chunk may be partial.
@@ -79,7 +81,7 @@ int build_plan(const Geometry& g, HostPlan* out, std::string* err) {
       it.kv1_begin = p.n_frame_rows;
       it.kv1_end = p.L;
       it.split = -1;
-      it.reserved = 0;
+      it.flags = 0;
       p.items.push_back(it);
     }
   }
@@ -105,7 +107,7 @@ int build_plan(const Geometry& g, HostPlan* out, std::string* err) {
         it.kv0_end = int32_t(std::min<int64_t>(p.L, (s + 1) * chunk));
         it.kv1_begin = it.kv1_end = 0;
         it.split = p.n_splits > 1 ? s : -1;
-        it.reserved = 0;
+        it.flags = 0;
         p.items.push_back(it);
       }
     }
@@ -113,7 +115,53 @@ int build_plan(const Geometry& g, HostPlan* out, std::string* err) {
       p.partial_bytes = int64_t(p.n_splits) * g.G * g.H * (g.d + 2) * int64_t(sizeof(float));
   }
 
-  // Launch order (see HostPlan::work).
+  build_launch_order(&p);
+  *out = std::move(p);
+  return 0;
+}
+
+int build_causal_plan(int n, int H, int d, HostPlan* out, std::string* err) {
+  if (n < 1 || H < 1) {
+    *err = "invalid causal geometry: need n, H >= 1";
+    return 1;
+  }
+  if (d != 64 && d != 128) {
+    *err = "unsupported head size d=" + std::to_string(d) + " (supported: 64, 128)";
+    return 2;
+  }
+  if (int64_t(n) * H * d >= (int64_t(1) << 31)) {
+    *err = "unsupported size: n*H*d must be below 2^31 elements";
+    return 2;
+  }
+  HostPlan p;
+  p.geo = Geometry{1, n, 0, 1, 0, H, d, 1};
+  p.L = n;
+  p.n_frame_rows = n;
+  p.n_chunks = 1;
+  p.block_m = kBlockM;
+  p.block_n = kBlockN;
+  p.kept_pairs_per_head = int64_t(n) * (n + 1) / 2;
+  for (int32_t q = 0; q < n; q += p.block_m) {
+    Item it;
+    it.q_begin = q;
+    it.q_end = std::min(n, q + p.block_m);
+    it.kv0_begin = 0;
+    it.kv0_end = it.q_end;
+    it.kv1_begin = it.kv1_end = 0;
+    it.split = -1;
+    it.flags = kItemCausal;
+    p.items.push_back(it);
+  }
+  p.n_window_items = int32_t(p.items.size());
+  build_launch_order(&p);
+  *out = std::move(p);
+  return 0;
+}
+
+// Launch order (see HostPlan::work).
+void build_launch_order(HostPlan* pp) {
+  HostPlan& p = *pp;
+  const Geometry& g = p.geo;
   const int32_t n_items = int32_t(p.items.size());
   std::vector<int32_t> win, glob;
   for (int32_t h = 0; h < g.H; ++h)
@@ -127,8 +175,6 @@ int build_plan(const Geometry& g, HostPlan* out, std::string* err) {
     for (int32_t j = 0; j < pw && size_t(x) * pw + j < win.size(); ++j) dst[j] = win[size_t(x) * pw + j];
     for (int32_t j = 0; j < pg && size_t(x) * pg + j < glob.size(); ++j) dst[pw + j] = glob[size_t(x) * pg + j];
   }
-  *out = std::move(p);
-  return 0;
 }
 
 }  // namespace wa

@@ -15,8 +15,10 @@ namespace wa {
 
 struct Geometry {
   int T, S, G, K, radius, H, d;
+  int causal = 0;  // 1: causal dense attention over S rows (T = 1, G = 0); see build_causal_plan
   bool operator==(const Geometry& o) const {
-    return T == o.T && S == o.S && G == o.G && K == o.K && radius == o.radius && H == o.H && d == o.d;
+    return T == o.T && S == o.S && G == o.G && K == o.K && radius == o.radius && H == o.H && d == o.d &&
+           causal == o.causal;
   }
 };
 
@@ -29,8 +31,9 @@ struct Item {  // one block_m-row query tile over up to two key segments (all he
   int32_t kv0_begin, kv0_end;
   int32_t kv1_begin, kv1_end;
   int32_t split;     // -1: final rows; s >= 0: partial result of key split s (global leg)
-  int32_t reserved;
+  int32_t flags;     // kItemCausal: query row r sees keys <= r only
 };
+constexpr int32_t kItemCausal = 1;
 static_assert(sizeof(Item) == 32, "Item is uploaded as 8 int32");
 
 struct HostPlan {
@@ -63,6 +66,10 @@ constexpr int kFineSplitRounds = 4;  // window units >= this many rounds of all 
 
 // Status codes mirror the C ABI (0 ok, 1 invalid, 2 unsupported).
 int build_plan(const Geometry& g, HostPlan* out, std::string* err);
+
+// Causal dense attention over n rows (the audio VAE's attention): no groups, one leg of
+// block_m-row items, item rows [q0, q1) over keys [0, q1) with kItemCausal set.
+int build_causal_plan(int n, int H, int d, HostPlan* out, std::string* err);
 
 // Chunk window [lo, hi] of chunk c (clipped to existing chunks).
 inline void chunk_window(int c, int n_chunks, int radius, int* lo, int* hi) {

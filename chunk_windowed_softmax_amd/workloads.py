@@ -16,6 +16,11 @@ are drawn with ``torch.randn(L, H, d, generator=g)`` in that order (fp32), then 
 to the workload dtype with round-to-nearest-even.  For the ragged workload, a further
 ``torch.randperm(L, generator=g)[:round(0.01 * L)]`` picks rows whose q and k are
 multiplied by 8 (exact in bf16) to stretch the softmax range.
+
+The ``audio_causal*`` workloads are the causal dense attention of the audio VAE (the
+prhub digest of sglang PR #34949, item 3): one sequence of L = S rows, row i attending to
+rows 0..i, fp32 inputs and outputs.  The page states no sequence length or head shape;
+16384 rows x 16 heads of 64 is a synthetic stand-in of long-clip scale.
 """
 
 from __future__ import annotations
@@ -39,6 +44,7 @@ class Workload:
     dtype: torch.dtype
     scaled_row_frac: float = 0.0
     description: str = ""
+    causal: bool = False  # causal dense attention over L = S rows (T = 1, G = 0)
 
     @property
     def L(self) -> int:
@@ -50,7 +56,7 @@ class Workload:
 
     def with_heads(self, H: int) -> "Workload":
         return Workload(self.name + f"_H{H}", self.T, self.S, self.G, self.K, self.radius, H, self.d,
-                        self.dtype, self.scaled_row_frac, self.description)
+                        self.dtype, self.scaled_row_frac, self.description, self.causal)
 
 
 WORKLOADS: Dict[str, Workload] = {
@@ -69,6 +75,14 @@ WORKLOADS: Dict[str, Workload] = {
                                    "1% of rows with q,k scaled x8, bf16"),
     "dense": Workload("dense", T=8, S=1024, G=0, K=1, radius=8, H=16, d=64, dtype=torch.bfloat16,
                       description="degenerate dense ViT case: radius >= chunk count, no globals, bf16"),
+    # Causal dense attention of the audio VAE (sglang PR #34949, item 3): fp32 in and out.
+    # The page gives no sequence length or head shape; these are synthetic stand-ins.
+    "audio_causal_small": Workload("audio_causal_small", T=1, S=1000, G=0, K=1, radius=0, H=2, d=64,
+                                   dtype=torch.float32, causal=True,
+                                   description="causal, 1000 rows, 2 heads of 64, fp32"),
+    "audio_causal": Workload("audio_causal", T=1, S=16384, G=0, K=1, radius=0, H=16, d=64,
+                             dtype=torch.float32, causal=True,
+                             description="causal, 16384 rows, 16 heads of 64, fp32 in/out"),
 }
 
 

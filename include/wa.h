@@ -66,7 +66,11 @@ typedef struct wa_plan_info_t {
   int64_t workspace_bytes;          /* device workspace of the global leg's partials */
   int32_t launch_xcds;              /* launch order: number of XCD queues ... */
   int32_t launch_per_xcd;           /* ... and entries per queue (see wa_plan_launch_order) */
+  int32_t causal;                   /* 1 for a wa_causal_plan_create plan */
 } wa_plan_info_t;
+
+/* Item flag bits (column WA_ITEM_FLAGS). */
+#define WA_ITEM_CAUSAL 1
 
 /* Columns of one row of wa_plan_items(). */
 enum {
@@ -77,7 +81,7 @@ enum {
   WA_ITEM_KV1_BEGIN,   /* second key segment [begin, end); empty when begin == end */
   WA_ITEM_KV1_END,
   WA_ITEM_SPLIT,       /* -1: writes normalised output rows; s >= 0: split s of the global leg */
-  WA_ITEM_RESERVED,
+  WA_ITEM_FLAGS,       /* bit 0 (WA_ITEM_CAUSAL): query row r sees keys <= r only */
   WA_ITEM_COLS
 };
 
@@ -98,6 +102,20 @@ enum {
  * range), WA_ERR_ALLOC.
  */
 int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan** out);
+
+/*
+ * wa_causal_plan_create -- plan for causal dense attention over n rows: query row i of
+ * every head attends to key rows 0..i, scale 1/sqrt(d).  This is the audio VAE's
+ * attention in the prhub digest of sglang PR #34949 ("H3 VAE attention via the native USP
+ * backend", item 3 and its CausalAttention listing): causal SDPA over q, k, v laid out as
+ * (B, N, heads, head_dim), run once per batch element here (B = 1, so [n, H, d]); with
+ * WA_F32 tensors wa_forward keeps that module's FP32 contract (fp32 in and out, the
+ * attention itself in bf16 with fp32 accumulation, as for its fused backends).
+ * Same cache, handle and error rules as wa_plan_create (n, H >= 1; d in {64, 128};
+ * n*H*d < 2^31).  wa_forward with this plan takes [n, H, d] tensors; the plan has no
+ * window groups (wa_plan_info reports n_groups = 0, causal = 1).
+ */
+int wa_causal_plan_create(int n, int H, int d, wa_plan** out);
 
 /*
  * wa_plan_release -- drop one reference.  The plan (and its device memory) is freed

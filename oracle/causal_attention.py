@@ -18,8 +18,9 @@ Readings taken where the page is silent (each also listed in the design doc):
 * Causal means query row i sees key rows 0..i (queries and keys have the same length,
   so the usual top-left alignment); the scale is SDPA's default 1/sqrt(head_dim).
 * The fused-backend contract is modelled as: fp32 inputs rounded to bf16 (RNE) for the
-  attention, fp32 output.  The oracle therefore takes the values the kernel consumes
-  (exactly upcast) and computes in float64.
+  attention, fp32 output.  The oracle computes in float64 from the exact input values,
+  so that rounding is part of the error the parity tolerance covers (as for the window
+  path's fp32 case).
 
 Every function is pinned by ``tests/test_oracle_causal.py``.
 """

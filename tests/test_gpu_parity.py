@@ -13,7 +13,8 @@ import pytest
 import torch
 
 from chunk_windowed_softmax_amd.workloads import WORKLOADS, make_custom_inputs, make_inputs
-from oracle import Geometry, window_attention_reference, window_attention_rows
+from oracle import (Geometry, causal_attention_reference, causal_attention_rows, window_attention_reference,
+                    window_attention_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -156,3 +157,69 @@ def test_rows_sum_to_one_and_fp32_output(gpu_lib):
     out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda())
     assert out.dtype == torch.float32
     assert (out - 1).abs().max().item() <= 4e-3
+
+
+# ---------------------------------------------------------------- causal (audio VAE)
+
+
+@pytest.mark.parametrize("n,H,d,dtype", [
+    (1, 1, 64, torch.float32),      # one row
+    (37, 2, 64, torch.float32),     # inside one key tile
+    (256, 2, 128, torch.bfloat16),  # exactly one work item
+    (300, 3, 64, torch.float32),    # ragged second item
+    (1000, 2, 64, torch.float32),   # several items, ragged tail
+    (777, 1, 128, torch.bfloat16),
+])
+def test_causal_parity(gpu_lib, n, H, d, dtype):
+    _say(f"causal parity n={n} H={H} d={d} {dtype}")
+    q, k, v = make_custom_inputs(n, H, d, dtype, seed=6)
+    plan = gpu_lib.wa_causal_plan_create(n, H, d)
+    out = gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    assert out.dtype == dtype and tuple(out.shape) == (n, H, d)
+    ref = causal_attention_reference(q, k, v)
+    rel, mx = _errors(out.float().cpu(), ref)
+    _say(f"causal n={n}: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+def test_audio_causal_sampled_parity(gpu_lib):
+    w = WORKLOADS["audio_causal"]
+    _say(f"audio_causal: L={w.L} H={w.H} d={w.d} fp32")
+    q, k, v = make_inputs(w, seed=0)
+    plan = gpu_lib.wa_causal_plan_create(w.L, w.H, w.d)
+    out = gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert out.dtype == torch.float32 and not torch.isnan(out).any()
+    rng = np.random.default_rng(7)
+    edges = [0, 1, 31, 32, 63, 64, 65, 255, 256, 257, 4095, 4096, w.L - 2, w.L - 1]
+    rows = np.unique(np.concatenate([rng.choice(w.L, 48, replace=False), edges]).astype(np.int64))
+    _say(f"audio_causal: oracle on {len(rows)} rows x {w.H} heads")
+    ref = causal_attention_rows(q, k, v, rows, range(w.H))
+    rel, mx = _errors(out[rows].float(), ref)
+    _say(f"audio_causal sampled: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
+def test_causal_cover_determinism_and_no_future_keys(gpu_lib):
+    """NaN prefill is fully overwritten, results repeat bit for bit, and perturbing rows
+    >= j of k and v leaves output rows < j bit-identical (future keys are never used)."""
+    n, H, d = 700, 2, 64
+    _say("causal cover / determinism / future keys")
+    q, k, v = (x.cuda() for x in make_custom_inputs(n, H, d, torch.bfloat16, seed=8))
+    plan = gpu_lib.wa_causal_plan_create(n, H, d)
+    out1 = torch.full_like(q, float("nan"))
+    gpu_lib.wa_forward(plan, q, k, v, out=out1)
+    out2 = torch.full_like(q, float("nan"))
+    gpu_lib.wa_forward(plan, q, k, v, out=out2)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out1).any() and torch.equal(out1, out2)
+    for j in (1, 100, 256, 321, 699):
+        k2, v2 = k.clone(), v.clone()
+        k2[j:] = 3.0
+        v2[j:] = -5.0
+        out3 = gpu_lib.wa_forward(plan, q, k2, v2)
+        torch.cuda.synchronize()
+        assert torch.equal(out3[:j], out1[:j]), j
+        assert not torch.equal(out3[j:], out1[j:]), j

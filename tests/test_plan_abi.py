@@ -167,3 +167,37 @@ def test_plan_cache_and_refcounts(lib):
     assert a.info == c.info
     for p in (a, b, c, *others):
         p.release()
+
+
+@pytest.mark.parametrize("n,H,d", [(1, 1, 64), (255, 2, 64), (256, 1, 128), (1000, 3, 64), (16384, 16, 64)])
+def test_causal_plan(lib, n, H, d):
+    """Causal plans: block_m-row items over keys [0, q_end) flagged causal, no groups, the
+    causal pair count, a full launch order."""
+    plan = wa.wa_causal_plan_create(n, H, d)
+    info = plan.info
+    assert info["causal"] == 1 and info["n_groups"] == 0 and info["L"] == n and info["n_splits"] == 0
+    assert info["kept_pairs_per_head"] == n * (n + 1) // 2
+    items = wa.wa_plan_items(plan)
+    bm = info["block_m"]
+    assert len(items) == (n + bm - 1) // bm
+    for j, it in enumerate(items):
+        q0, q1, a0, b0, a1, b1, split, flags = (int(x) for x in it)
+        assert (q0, q1) == (j * bm, min(n, (j + 1) * bm))
+        assert (a0, b0, a1, b1, split, flags) == (0, q1, 0, 0, -1, 1)
+    assert len(wa.wa_plan_groups(plan)) == 0
+    _check_launch_order(plan, H)
+    # distinct from the window plan of the same shape, and cached
+    assert wa.wa_plan_create(1, n, 0, 1, 0, H, d).info["causal"] == 0
+    again = wa.wa_causal_plan_create(n, H, d)
+    assert again.handle.value == plan.handle.value
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 1, 64), wa.WA_ERR_INVALID), ((4, 0, 64), wa.WA_ERR_INVALID),
+    ((4, 1, 96), wa.WA_ERR_UNSUPPORTED), ((1 << 20, 32, 128), wa.WA_ERR_UNSUPPORTED),
+])
+def test_causal_plan_errors(lib, args, code):
+    with pytest.raises(wa.WaError) as e:
+        wa.wa_causal_plan_create(*args)
+    assert e.value.code == code
+    assert lib.wa_causal_plan_create(4, 1, 64, None) == wa.WA_ERR_INVALID
