@@ -31,7 +31,9 @@
 //   one matrix op at a time, so the vector ALU and LDS work hides under the matrix pipe.
 //   K/V tiles stream through a 4-deep LDS ring filled by direct global->LDS 16-byte loads
 //   (no registers, no LDS write instructions), issued three tiles ahead and spread over
-//   the matrix ops; one barrier per tile.  LDS rows hold d bf16; 16-byte chunks are
+//   the matrix ops; one barrier per tile.  The loads go through range-checked buffer
+//   resources, so a tile costs one scalar row offset and one add per slice, with no
+//   per-lane clamping at segment or tensor ends.  LDS rows hold d bf16; 16-byte chunks are
 //   XOR-swizzled per row (applied on the global side of the DMA) so the K reads and the
 //   transpose reads are free of bank conflicts.
 //   The running max is raised lazily: exponentials are taken against the running max,
@@ -59,6 +61,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kNW = 4;         // waves per block, one per SIMD
 constexpr int kWaveRows = 64;  // query rows per wave (two 32-row blocks)
@@ -109,8 +112,13 @@ struct AttnParams {
   float* __restrict__ part_o;
   float* __restrict__ part_ml;
   int H, G, frame_rows, n_items, total, per_xcd;
+  uint32_t tensor_bytes;  // bytes of one of q/k/v: L * H * D * 2
   float scale_log2;
 };
+
+// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle, so each
+// access of a lane is range checked against num_records (word 2) and reads 0 past it.
+constexpr int32_t kBufferWord3 = 0x00020000;
 
 // One block = 4 waves (one per SIMD); one wave = 64 query rows as two 32-row blocks
 // (qb = 0, 1).  Every K and V fragment read from LDS feeds both blocks' matrix ops.
@@ -166,12 +174,24 @@ void attn_kernel(AttnParams p) {
   // chunk (j*64 + lane), i.e. row m/CH, physical chunk m%CH, which holds the logical chunk
   // (physical ^ swz(row)) of that key row.
   // Slice i of a lane lies RPI rows below slice 0 and has the same swizzle (the swizzle
-  // depends on row % 16 and RPI is a multiple of 16), so one base offset serves all slices.
+  // depends on row % 16 and RPI is a multiple of 16).  The loads go through buffer
+  // resources based at this head's first element: each lane's offset is its slice offset
+  // plus the tile's row offset, range checked against the end of the tensor (rows past it
+  // read as zero; they only ever land in masked key rows).
   constexpr int RPI = kNW * 64 / CH;  // tile rows between consecutive slices of one wave
   static_assert(RPI % 16 == 0, "slices of one lane must share the row swizzle");
   const uint32_t dma_row0 = uint32_t((wave * 64 + lane) / CH);
-  // the lane's byte offset within a key row: head, then the swizzled 16-byte chunk
-  const uint32_t dma_lane = uint32_t(h * D * 2) + uint32_t((((wave * 64 + lane) % CH) ^ swz<D>(dma_row0)) * 16);
+  uint32_t dma_off[JPW];  // byte offset of the lane's 16 bytes of slice i within a tile
+#pragma unroll
+  for (int i = 0; i < JPW; ++i)
+    dma_off[i] = (dma_row0 + uint32_t(i * RPI)) * row_bytes +
+                 uint32_t((((wave * 64 + lane) % CH) ^ swz<D>(dma_row0)) * 16);
+  auto make_rsrc = [&](const uint16_t* t) __attribute__((always_inline)) -> i32x4 {
+    const uint64_t a = reinterpret_cast<uint64_t>(t) + uint64_t(h) * (D * 2);
+    return i32x4{int32_t(uint32_t(a)), int32_t(uint32_t(a >> 32) & 0xFFFF),
+                 int32_t(p.tensor_bytes - uint32_t(h) * (D * 2)), kBufferWord3};
+  };
+  const i32x4 rsrc_k = make_rsrc(p.k), rsrc_v = make_rsrc(p.v);
 
   // ---- LDS read offsets (bytes within a tile)
   uint32_t koff[KS];  // K fragment (key row l32 of a 32-key block, chunk 2s+hh)
@@ -204,28 +224,30 @@ void attn_kernel(AttnParams p) {
     }
   };
 
-  // DMA load `idx` (slice idx / 2, K for even idx and V for odd) of tile u into ring slot
-  // u % NBUF.  Tiles past the last one re-load the last tile (into a slot nobody reads), so
-  // every tile issues the same number of loads.  Rows past the segment end re-read the
-  // segment's last row (finite data, masked out of the softmax), so no key outside the
-  // item's kept set is ever read.
-  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
-  auto dma_load = [&](int u, int idx) __attribute__((always_inline)) {
-    const int uu = u < nt ? u : nt - 1;
+  // Row offset (bytes) of the first key row of tile u.  Tiles past the last one re-load the
+  // last tile (into a slot nobody reads), so every tile issues the same number of loads.
+  // Rows past a segment end are the next rows of the tensor (finite data, masked out of the
+  // softmax) or, past the tensor, zeros.
+  auto tile_off = [&](int u) __attribute__((always_inline)) -> uint32_t {
     int n0, nend;
-    tile_range(uu, n0, nend);
+    tile_range(u < nt ? u : nt - 1, n0, nend);
+    return uint32_t(n0) * row_bytes;
+  };
+  // DMA load `idx` (slice idx / 2, K for even idx and V for odd) of the tile at row offset
+  // `toff` into ring slot u % NBUF.
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
+  auto dma_load = [&](int u, int idx, uint32_t toff) __attribute__((always_inline)) {
     const int i = idx >> 1;
-    const unsigned char* g = reinterpret_cast<const unsigned char*>((idx & 1) ? p.v : p.k) + (int64_t)n0 * row_bytes;
     const uint32_t l = lds_base + uint32_t((2 * (u % NBUF) + (idx & 1)) * TILEB + (i * kNW + wave) * 1024);
-    // rows past the segment end re-read its last row (branch-free; 24-bit multiply)
-    const uint32_t last = uint32_t(nend - 1 - n0 < kBN - 1 ? nend - 1 - n0 : kBN - 1);
-    const uint32_t row = dma_row0 + uint32_t(i * RPI);
-    const uint32_t off = dma_lane + __umul24(row < last ? row : last, row_bytes);
+    const uint32_t off = dma_off[i] + toff;
     // Issued as asm: the compiler would otherwise make the next LDS read of any buffer wait
     // for every DMA in flight (it cannot tell the ring slots apart).  Completion is ordered
     // by the explicit vmcnt waits before each barrier.  M0 holds the LDS destination (set
     // by the compiler through the operand; the nop covers the M0-write-to-DMA hazard).
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(g), "{m0}"(l) : "memory");
+    if (idx & 1)
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(rsrc_v), "{m0}"(l) : "memory");
+    else
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(off), "s"(rsrc_k), "{m0}"(l) : "memory");
   };
   constexpr int NLD = 2 * JPW;  // DMA loads per tile per wave
 
@@ -364,7 +386,9 @@ void attn_kernel(AttnParams p) {
   // PV runs after the loop.
   // P pairs are staged: pair k's FMAs issue at step fs(k), its exponentials one step later,
   // its bf16 packing one step after that and its row-sum dot one more step later, so no
-  // vector op waits on the one before it.
+  // vector op waits on the one before it.  Each stage's result is pinned at its step (an
+  // empty asm that reads it): without the pins the compiler sinks pure arithmetic next to
+  // its first use, which puts dependent vector ops back to back.
   // The fast path needs no tile max: any P above 2^8 (a score more than 2^8 above the
   // running max, in exp2 units) makes this lane's row sum exceed 2^8, and that (or the first
   // tile, or a masked tile) sends the block to the slow path, which finds the max.
@@ -390,15 +414,20 @@ void attn_kernel(AttnParams p) {
       const int fs = k * N / 8;
       const int n = lo + k, b = n >> 3, e = 2 * (n & 7);
       if (fs + 3 == i) rs[qb][k & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[qb][n], kOnes2, rs[qb][k & 1], false);
-      if (fs + 2 == i) pw[qb][n] = cvt_bf16x2(fa[k], fb[k]);
+      if (fs + 2 == i) {
+        pw[qb][n] = cvt_bf16x2(fa[k], fb[k]);
+        asm volatile("" ::"v"(pw[qb][n]));
+      }
       if (fs + 1 == i) {
         fa[k] = fast_exp2(fa[k]);
         fb[k] = fast_exp2(fb[k]);
+        asm volatile("" ::"v"(fa[k]), "v"(fb[k]));
       }
       if (fs == i) {
         const float x0 = sa[b][e], x1 = sa[b][e + 1];
         fa[k] = __builtin_fmaf(x0, c2, -mc[qb]);
         fb[k] = __builtin_fmaf(x1, c2, -mc[qb]);
+        asm volatile("" ::"v"(fa[k]), "v"(fb[k]));
       }
     }
   };
@@ -447,8 +476,11 @@ void attn_kernel(AttnParams p) {
   // prologue: tile 0 and the Q fragments land together (the explicit wait also tells the
   // compiler that Q is complete, so it adds no wait inside the loop); then tiles 1 and the
   // first half of 2 go in flight.
+  {
+    const uint32_t toff0 = tile_off(0);
 #pragma unroll
-  for (int idx = 0; idx < NLD; ++idx) dma_load(0, idx);
+    for (int idx = 0; idx < NLD; ++idx) dma_load(0, idx, toff0);
+  }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const int qrow = row0 + 32 * qb + l32;
@@ -462,10 +494,12 @@ void attn_kernel(AttnParams p) {
     }
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  uint32_t toff_a = tile_off(1);  // the tile whose DMA is in flight in two halves
 #pragma unroll
-  for (int idx = 0; idx < NLD; ++idx) dma_load(1, idx);
+  for (int idx = 0; idx < NLD; ++idx) dma_load(1, idx, toff_a);
+  toff_a = tile_off(2);
 #pragma unroll
-  for (int idx = 0; idx < NLD / 2; ++idx) dma_load(2, idx);
+  for (int idx = 0; idx < NLD / 2; ++idx) dma_load(2, idx, toff_a);
   barrier();
   if (wave_active) {
 #pragma unroll
@@ -488,7 +522,7 @@ void attn_kernel(AttnParams p) {
       // slot 0
       s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
         stage_at(1, s1, 8, NS, i);
-        if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)));
+        if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)), toff_a);
       });
       check_block(1, s1, valid_prev, n0_prev, t == 1);
       // slot 1
@@ -507,11 +541,12 @@ void attn_kernel(AttnParams p) {
       check_block(0, s0, valid, n0, t == 0);
     } else {
 #pragma unroll
-      for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx);
+      for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx, toff_a);
     }
 
     WA_WAIT_VMCNT(NLD);  // tile t+1 has landed (tile t+2 may still be in flight) ...
     barrier();           // ... for every wave
+    toff_a = tile_off(t + 3);
 
     if (wave_active) {
       // slot 3 (after the last tile the K reads hit a buffer nobody uses)
@@ -520,7 +555,7 @@ void attn_kernel(AttnParams p) {
         if (i < NP) {
 #pragma unroll
           for (int r = 0; r < 2 * KS / NP; ++r) read_k(i * (2 * KS / NP) + r);
-          if (i % (NP / (NLD / 2)) == 0) dma_load(t + 3, i / (NP / (NLD / 2)));
+          if (i % (NP / (NLD / 2)) == 0) dma_load(t + 3, i / (NP / (NLD / 2)), toff_a);
         }
         stage_at(1, s1, 0, NP, i);
       });
@@ -528,7 +563,7 @@ void attn_kernel(AttnParams p) {
       for (int st = 0; st < KS; ++st) koff[st] += step_k;
     } else {
 #pragma unroll
-      for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx);
+      for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
     }
     valid_prev = valid;
     n0_prev = n0;
@@ -657,6 +692,7 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   p.per_xcd = a.work_per_xcd;
   p.total = kXcds * a.work_per_xcd;
   p.scale_log2 = a.scale_log2;
+  p.tensor_bytes = uint32_t(a.L) * uint32_t(a.H) * uint32_t(D * 2);
   const int grid = p.per_xcd * kXcds;
   hipLaunchKernelGGL((attn_kernel<D, OUT_F32>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();

@@ -135,7 +135,9 @@ int wa_plan_release(wa_plan* plan);
  * synchronising.  The first call on a device allocates the plan's device tables and
  * workspace (and, for WA_F32, a bf16 staging copy of q, k, v); later calls allocate
  * nothing.  Concurrent calls with one plan on different streams race on the plan's
- * workspace: serialise them.
+ * workspace: serialise them.  Every element of q, k and v must be finite: key tiles are
+ * read whole, so rows next to a row's kept keys are read and masked to zero weight, and a
+ * NaN or infinity there would still reach the output (finite values never do).
  * Errors: WA_ERR_INVALID (NULL / misaligned / overlapping pointers, bad dtype),
  * WA_ERR_ALLOC, WA_ERR_HIP (launch failure).
  */
