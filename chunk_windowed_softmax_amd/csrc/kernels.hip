@@ -301,14 +301,28 @@ void attn_kernel(AttnParams p) {
                                    __builtin_shufflevector(pw[qb][n + 2], pw[qb][n + 3], 0, 1, 2, 3), 0, 1, 2, 3,
                                    4, 5, 6, 7);
   };
-  // Row sums of exactly the rounded P that multiplies V (v_dot2 with (1, 1)), so the
-  // weights applied to V sum to one; two accumulation chains per block, this lane's keys.
+  // Row sums of exactly the rounded P that multiplies V, so the weights applied to V sum to
+  // one (with one dominant key the output is then that key's value row, whatever its
+  // rounding); two fp32 accumulation chains per block over this lane's keys.  A pair is
+  // added either by one v_dot2 against (1, 1) or by widening its two bf16 halves (a shift
+  // and a mask) and two fp32 adds.  Measured per slot: beside the S matrix ops (operands in
+  // AGPRs) a dot op stalls the matrix pipe for about 13 cycles while the four plain ops
+  // issue for free; beside the PV matrix ops the single dot op is the cheaper one.
   float rs[2][2];
-  // One pair of P against the given max.
+  auto add_pair = [&](int qb, bf16x2 w) __attribute__((always_inline)) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, w);
+    rs[qb][0] += __builtin_bit_cast(float, u << 16);
+    rs[qb][1] += __builtin_bit_cast(float, u & 0xFFFF0000u);
+  };
+  auto dot_pair = [&](int qb, int k, bf16x2 w) __attribute__((always_inline)) {
+    rs[qb][k & 1] = __builtin_amdgcn_fdot2_f32_bf16(w, kOnes2, rs[qb][k & 1], false);
+  };
+  // One pair of P against the given max, and its row sums.
   auto p_pair = [&](int qb, const f32x16 (&sa)[2], int n, float mcq) __attribute__((always_inline)) {
     const int b = n >> 3, e = 2 * (n & 7);
     const float x0 = sa[b][e], x1 = sa[b][e + 1];
     pw[qb][n] = cvt_bf16x2(fast_exp2(__builtin_fmaf(x0, c2, -mcq)), fast_exp2(__builtin_fmaf(x1, c2, -mcq)));
+    add_pair(qb, pw[qb][n]);
   };
   // Value of the lane 32 apart (the other half of the same query's keys), in both orders.
   auto other_half = [](float x) __attribute__((always_inline)) -> f32x2 {
@@ -363,10 +377,7 @@ void attn_kernel(AttnParams p) {
     }
     rs[qb][0] = rs[qb][1] = 0.f;
 #pragma unroll
-    for (int n = 0; n < 16; ++n) {
-      p_pair(qb, sa, n, mc[qb]);
-      rs[qb][n & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[qb][n], kOnes2, rs[qb][n & 1], false);
-    }
+    for (int n = 0; n < 16; ++n) p_pair(qb, sa, n, mc[qb]);
   };
 
   // ---- Software pipeline over 64-key tiles, one "slot" = one group of matrix ops with a
@@ -385,10 +396,12 @@ void attn_kernel(AttnParams p) {
   // is empty (scores -inf, V zero), so every iteration runs the same code; block 1's last
   // PV runs after the loop.
   // P pairs are staged: pair k's FMAs issue at step fs(k), its exponentials one step later,
-  // its bf16 packing one step after that and its row-sum dot one more step later, so no
-  // vector op waits on the one before it.  Each stage's result is pinned at its step (an
-  // empty asm that reads it): without the pins the compiler sinks pure arithmetic next to
-  // its first use, which puts dependent vector ops back to back.
+  // its bf16 packing and its row sums in the next steps (see stage_at); beside the S
+  // matrix ops the packing waits two steps, since an op that reads a fresh exp2 result one
+  // matrix op later stalls there.
+  // Each stage's result is pinned at its step (an empty asm that reads it): without the
+  // pins the compiler sinks pure arithmetic next to its first use, which puts dependent
+  // vector ops back to back.
   // The fast path needs no tile max: any P above 2^8 (a score more than 2^8 above the
   // running max, in exp2 units) makes this lane's row sum exceed 2^8, and that (or the first
   // tile, or a masked tile) sends the block to the slow path, which finds the max.
@@ -407,14 +420,25 @@ void attn_kernel(AttnParams p) {
   const f32x16 zero = {};
   float fa[8], fb[8];  // staged pair values
 
-  // stage work of pairs [lo, lo + 8) of block qb at step i of an N-step slot
+  // stage work of pairs [lo, lo + 8) of block qb at step i of an N-step slot.  Pairs 0..7
+  // run beside PV matrix ops (packing at fs + 2, one v_dot2 at fs + 3), pairs 8..15 beside
+  // S matrix ops (packing at fs + 3, shift/mask/add row sums at fs + 4).
   auto stage_at = [&](int qb, const f32x16 (&sa)[2], int lo, int N, int i) __attribute__((always_inline)) {
+    const bool pv = lo == 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       const int fs = k * N / 8;
       const int n = lo + k, b = n >> 3, e = 2 * (n & 7);
-      if (fs + 3 == i) rs[qb][k & 1] = __builtin_amdgcn_fdot2_f32_bf16(pw[qb][n], kOnes2, rs[qb][k & 1], false);
-      if (fs + 2 == i) {
+      const int f_pack = pv ? fs + 2 : fs + 3, f_sum = f_pack + 1;
+      if (f_sum == i) {
+        if (pv) {
+          dot_pair(qb, k, pw[qb][n]);
+        } else {
+          add_pair(qb, pw[qb][n]);
+          asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
+        }
+      }
+      if (f_pack == i) {
         pw[qb][n] = cvt_bf16x2(fa[k], fb[k]);
         asm volatile("" ::"v"(pw[qb][n]));
       }
@@ -440,10 +464,14 @@ void attn_kernel(AttnParams p) {
     l_run[qb] += rs[qb][0] + rs[qb][1];
     __builtin_amdgcn_sched_barrier(0);
   };
-  // PV slot of block qb: N matrix ops (when `mma`), then three tail steps for the staged pairs.
+  // Steps after the last matrix op of a slot in which the staged pairs finish: the last pair
+  // starts at step 7 * N / 8 and ends at most 4 steps later (N = NS = NP).
+  static_assert(NS == NP, "S and PV slots have the same number of steps");
+  constexpr int kTail = 7 * NS / 8 + 5 - NS;
+  // PV slot of block qb: N matrix ops (when `mma`), then the tail steps for the staged pairs.
   auto pv_slot = [&](int qb, bool mma, auto&& extra) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NP + 3; ++i) {
+    for (int i = 0; i < NP + kTail; ++i) {
       if (mma && i < NP) {
         const int b = i / (2 * DB), tt = (i / DB) & 1, db = i % DB;
         oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(b, tt, db), pfrag(qb, b, tt), oacc[qb][db], 0, 0, 0);
@@ -454,7 +482,7 @@ void attn_kernel(AttnParams p) {
   };
   auto s_slot = [&](int qb, f32x16 (&sa)[2], bool mma, auto&& extra) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NS + 3; ++i) {
+    for (int i = 0; i < NS + kTail; ++i) {
       if (mma && i < NS) {
         const int st = i >> 1, b = i & 1;
         sa[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st][b], qf[qb][st], st == 0 ? zero : sa[b], 0, 0, 0);
