@@ -253,13 +253,16 @@ void attn_kernel(AttnParams p) {
 
   const float c2 = p.scale_log2;
   const float lazy_raw = kLazyLog2 / c2;
+  // Initial running max: finite (every weight against it is zero, and every finite score
+  // exceeds it by more than 2^8, so the first tile, which takes the slow path, raises it).
+  constexpr float kMaxInit = -0x1p100f;
 
   float m_run[2], mc[2], l_run[2];  // running max of raw scores (this lane's queries), * c2, sum
   f32x16 oacc[2][DB];
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    m_run[qb] = -__builtin_inff();
-    mc[qb] = 0.f;
+    m_run[qb] = kMaxInit;
+    mc[qb] = kMaxInit * c2;
     l_run[qb] = 0.f;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
