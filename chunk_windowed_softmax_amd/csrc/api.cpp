@@ -33,6 +33,7 @@ struct DeviceResources {
   float* part = nullptr;     // partial O then partial (m, l) of the global leg
   void* staging = nullptr;   // bf16 copies of fp32 q, k, v (allocated on first fp32 call)
   int64_t staging_bytes = 0;
+  int n_cus = 0;             // compute units of the device: one persistent block each
 };
 
 }  // namespace
@@ -79,14 +80,18 @@ int device_resources(wa_plan* p, DeviceResources** out) {
     return WA_OK;
   }
   DeviceResources r;
-  // items, then the launch order (int32), in one allocation
+  e = hipDeviceGetAttribute(&r.n_cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || r.n_cus < 1) return fail(WA_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
+  // items, then the launch order (int32), then the work-queue counters, in one allocation
   const size_t item_bytes = p->host.items.size() * sizeof(wa::Item);
   const size_t work_bytes = p->host.work.size() * sizeof(int32_t);
-  e = hipMalloc(&r.items, item_bytes + work_bytes);
+  const size_t counter_bytes = (wa::kXcdCount + 1) * sizeof(int32_t);
+  e = hipMalloc(&r.items, item_bytes + work_bytes + counter_bytes);
   if (e != hipSuccess) return fail(WA_ERR_ALLOC, std::string("hipMalloc(items): ") + hipGetErrorString(e));
   e = hipMemcpy(r.items, p->host.items.data(), item_bytes, hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(reinterpret_cast<char*>(r.items) + item_bytes, p->host.work.data(), work_bytes, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(reinterpret_cast<char*>(r.items) + item_bytes + work_bytes, 0, counter_bytes);
   if (e != hipSuccess) {
     (void)hipFree(r.items);
     return fail(WA_ERR_HIP, std::string("hipMemcpy(items): ") + hipGetErrorString(e));
@@ -310,6 +315,12 @@ int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v
   a.n_items = (int)h.items.size();
   a.work = reinterpret_cast<const int32_t*>(r->items + h.items.size());
   a.work_per_xcd = h.work_per_xcd;
+  a.counters = const_cast<int32_t*>(a.work) + h.work.size();
+  // Persistent blocks pay a few memory round trips per unit for the queues; they pay off only
+  // when each CU runs several units.  Otherwise one block per unit.
+  const int64_t units = int64_t(h.items.size()) * h.geo.H;
+  a.persistent = units > 2 * int64_t(r->n_cus) ? 1 : 0;
+  a.grid = a.persistent ? r->n_cus : wa::kXcdCount * h.work_per_xcd;
   a.n_splits = h.n_splits;
   a.part_o = r->part;
   a.part_ml = r->part ? r->part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;

@@ -40,10 +40,11 @@
 //   and a wave-uniform slow path raises it (rescaling the accumulators) only when some
 //   row's max grew by more than 2^8 (values up to 2^8 are exact in the softmax ratio);
 //   the same path masks keys past a segment end.
-//   Blocks take their work unit from the plan's launch-order table: each XCD (blocks are
-//   dispatched round-robin over the XCDs) gets a contiguous run of window units, so the
-//   query tiles of one group run side by side and share that XCD's L2, followed by its
-//   share of the shorter global-leg units, which even out the end of the launch.
+//   The launch is persistent: one block per CU takes work units from its XCD's queue in the
+//   plan's launch order (blocks are dispatched round-robin over the XCDs), a contiguous run
+//   of window units, so the query tiles of one group run side by side and share that XCD's
+//   L2, followed by its share of the shorter global-leg units.  A block whose queue is empty
+//   takes units from the other XCDs' queues, which evens out the end of the launch.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -109,12 +110,48 @@ struct AttnParams {
   void* __restrict__ out;
   const Item* __restrict__ items;
   const int32_t* __restrict__ work;
+  int32_t* __restrict__ counters;  // kXcds queue counters, then the count of finished blocks
+  int persistent;                   // 0: block b runs unit work[(b % 8) * per_xcd + b / 8] only
   float* __restrict__ part_o;
   float* __restrict__ part_ml;
   int H, G, frame_rows, n_items, total, per_xcd;
   uint32_t tensor_bytes;  // bytes of one of q/k/v: L * H * D * 2
   float scale_log2;
 };
+
+// Next work unit for a block on XCD `xcd`, run by one whole wave: its own XCD's queue first
+// (the queue rows of the launch order: window units, then global-leg units, then -1
+// padding), then the other XCDs' queues (work stealing at the end of the launch).  -1 when
+// every queue is empty.  A queue counter that has passed the queue's last unit marks it
+// empty; lanes 0..7 probe all eight queues at once, so a block that runs out costs two
+// round trips to memory, not eight.
+__device__ __forceinline__ int fetch_unit(const int32_t* __restrict__ work, int32_t* __restrict__ counters,
+                                          int per_xcd, int xcd, int lane) {
+  int u = -1;
+  if (lane == 0) {
+    const int i = atomicAdd(counters + xcd, 1);
+    if (i < per_xcd) u = work[xcd * per_xcd + i];
+  }
+  u = __builtin_amdgcn_readfirstlane(u);
+  while (u < 0) {
+    const int y = lane & (kXcdCount - 1);
+    const int x = xcd + y < kXcdCount ? xcd + y : xcd + y - kXcdCount;
+    bool open = false;
+    if (lane < kXcdCount) {
+      const int c = __hip_atomic_load(counters + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      open = c < per_xcd && work[x * per_xcd + c] >= 0;
+    }
+    const uint64_t m = __builtin_amdgcn_ballot_w64(open);
+    if (m == 0) break;  // every queue is empty
+    const int x0 = (xcd + __builtin_ctzll(m)) % kXcdCount;
+    if (lane == 0) {
+      const int i = atomicAdd(counters + x0, 1);
+      if (i < per_xcd) u = work[x0 * per_xcd + i];
+    }
+    u = __builtin_amdgcn_readfirstlane(u);
+  }
+  return u;
+}
 
 // Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle, so each
 // access of a lane is range checked against num_records (word 2) and reads 0 past it.
@@ -156,9 +193,11 @@ void attn_kernel(AttnParams p) {
   const int hh = lane >> 5;     // half of the wave: k sub-block of the MFMA operands
   const int l32 = lane & 31;
 
-  const int bid = blockIdx.x;
-  const int unit = p.work[(bid % kXcds) * p.per_xcd + bid / kXcds];
-  if (unit < 0) return;
+  // Persistent blocks, one per CU: each runs work units (fetch_unit) until all queues are
+  // empty.  Blocks are dispatched round-robin over the XCDs.
+  const int xcd = blockIdx.x % kXcds;
+  __shared__ int s_unit;
+  auto run_item = [&](const int unit) __attribute__((always_inline)) {
   const int h = unit / p.n_items;
   const Item it = p.items[unit - h * p.n_items];
   const int H = p.H;
@@ -660,6 +699,30 @@ void attn_kernel(AttnParams p) {
       }
     }
   }
+  };  // run_item
+
+  for (int n = 0;; ++n) {
+    // The barrier also orders this block's LDS use: every wave has finished the previous
+    // unit (its DMA drained, its reads done) before the next unit's prologue refills the ring.
+    // Without queues (few units) block b runs the one unit at its place in the launch order.
+    if (wave == 0) {
+      const int u = p.persistent ? fetch_unit(p.work, p.counters, p.per_xcd, xcd, lane)
+                                 : (n == 0 ? p.work[xcd * p.per_xcd + int(blockIdx.x) / kXcds] : -1);
+      if (lane == 0) s_unit = u;
+    }
+    __syncthreads();
+    const int unit = __builtin_amdgcn_readfirstlane(s_unit);
+    if (unit < 0) break;
+    run_item(unit);
+  }
+  // The last block to finish resets the queue counters for the next launch (every block has
+  // made its last fetch when it counts itself finished).
+  if (p.persistent && tid == 0) {
+    __threadfence();
+    if (atomicAdd(p.counters + kXcds, 1) == int(gridDim.x) - 1) {
+      for (int x = 0; x <= kXcds; ++x) atomicExch(p.counters + x, 0);
+    }
+  }
 }
 
 // Merge the global leg's key splits: for each (global row, head), with m_s in log2 units,
@@ -720,11 +783,13 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   p.frame_rows = a.frame_rows;
   p.n_items = a.n_items;
   p.work = a.work;
+  p.counters = a.counters;
+  p.persistent = a.persistent;
   p.per_xcd = a.work_per_xcd;
   p.total = kXcds * a.work_per_xcd;
   p.scale_log2 = a.scale_log2;
   p.tensor_bytes = uint32_t(a.L) * uint32_t(a.H) * uint32_t(D * 2);
-  const int grid = p.per_xcd * kXcds;
+  const int grid = a.grid;
   hipLaunchKernelGGL((attn_kernel<D, OUT_F32>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -21,6 +21,9 @@ struct ForwardArgs {
   int n_items;
   const int32_t* work;    // device copy of the launch order (kXcdCount * work_per_xcd units)
   int work_per_xcd;
+  int32_t* counters;      // kXcdCount + 1 device counters, zero between launches
+  int persistent;         // 1: `grid` blocks (one per compute unit) run the queues
+  int grid;               // blocks to launch
   int n_splits;           // > 1: global-leg items write partials, then a combine pass
   float* part_o;          // [n_splits, G, H, d] fp32
   float* part_ml;         // [n_splits, G, H, 2] fp32: running max (log2 units), row sum

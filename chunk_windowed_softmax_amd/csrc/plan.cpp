@@ -172,8 +172,9 @@ void build_launch_order(HostPlan* pp) {
   p.work.assign(size_t(kXcdCount) * p.work_per_xcd, -1);
   for (int x = 0; x < kXcdCount; ++x) {
     int32_t* dst = p.work.data() + size_t(x) * p.work_per_xcd;
-    for (int32_t j = 0; j < pw && size_t(x) * pw + j < win.size(); ++j) dst[j] = win[size_t(x) * pw + j];
-    for (int32_t j = 0; j < pg && size_t(x) * pg + j < glob.size(); ++j) dst[pw + j] = glob[size_t(x) * pg + j];
+    int32_t n = 0;  // units are packed at the front of the row; -1 padding only at its end
+    for (int32_t j = 0; j < pw && size_t(x) * pw + j < win.size(); ++j) dst[n++] = win[size_t(x) * pw + j];
+    for (int32_t j = 0; j < pg && size_t(x) * pg + j < glob.size(); ++j) dst[n++] = glob[size_t(x) * pg + j];
   }
 }
 

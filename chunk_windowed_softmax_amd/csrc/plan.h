@@ -45,10 +45,11 @@ struct HostPlan {
   std::vector<Group> groups;
   std::vector<Item> items;  // window items (group-major), then global-leg items (split-major)
   int64_t partial_bytes = 0;  // device workspace of the global leg's partial results
-  // Launch order: entry b of XCD x (block x + 8 b) is unit work[x * work_per_xcd + b], unit =
-  // head * items.size() + item, or -1 (no work).  Each XCD gets a contiguous run of window
-  // units (same group's query tiles side by side, sharing its L2) and then a run of the
-  // shorter global-leg units, so the last blocks to start are the short ones.
+  // Launch order: one work queue per XCD; row x holds units work[x * work_per_xcd + i], unit =
+  // head * items.size() + item, packed at the front, then -1 padding.  Each XCD's queue is a
+  // contiguous run of window units (same group's query tiles side by side, sharing its L2)
+  // and then a run of the shorter global-leg units, so the last units to start are the short
+  // ones; blocks that empty their own queue take units from the other XCDs' queues.
   std::vector<int32_t> work;
   int32_t work_per_xcd = 0;
 };

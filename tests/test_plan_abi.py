@@ -58,7 +58,8 @@ def _check_plan_against_oracle(T, S, G, K, r, H, d):
 
 def _check_launch_order(plan, H):
     """The launch order runs every (head, item) unit exactly once; per XCD queue the window
-    units come first, in increasing order (a contiguous run), then the global-leg units."""
+    units come first, in increasing order (a contiguous run), then the global-leg units, all
+    packed at the front of the row (the kernel's queues stop at the first -1)."""
     info = plan.info
     order = wa.wa_plan_launch_order(plan)
     assert order.shape == (info["launch_xcds"], info["launch_per_xcd"])
@@ -69,6 +70,7 @@ def _check_launch_order(plan, H):
     assert sorted(units.tolist()) == list(range(H * n_items))
     for queue in order:
         q = queue[queue >= 0]
+        assert (queue[:len(q)] >= 0).all() and (queue[len(q):] == -1).all()
         is_win = (q % n_items) < n_window
         k = int(is_win.sum())
         assert is_win[:k].all() and not is_win[k:].any()
