@@ -61,7 +61,7 @@ constexpr int kXcdCount = 8;  // MI355X: workgroups are dispatched round-robin o
 // about 1/kGlobalSplitDiv of the longest window item: the short units finish each XCD's
 // queue and even out the tail of the launch.  Otherwise one split is about as long as the
 // longest window item (fewer partial results to merge).
-constexpr int kGlobalSplitDiv = 3;
+constexpr int kGlobalSplitDiv = 2;
 constexpr int kComputeUnits = 256;   // MI355X
 constexpr int kFineSplitRounds = 4;  // window units >= this many rounds of all compute units
 
