@@ -185,7 +185,9 @@ void attn_kernel(AttnParams p) {
   constexpr float kRowSumLimit = 256.f;         // fast path only while this lane's row sum <= 2^8
 
   constexpr int NBUF = 4;                       // LDS ring of (K, V) tile pairs
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[NBUF * 2 * TILEB];  // K0 V0 K1 V1 ...
+  constexpr int RINGB = NBUF * 2 * TILEB;       // bytes of the ring
+  constexpr int STAGEB = 8192;                  // per-wave output staging area after the ring
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[RINGB + kNW * STAGEB];  // K0 V0 K1 V1 ... stages
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -196,7 +198,9 @@ void attn_kernel(AttnParams p) {
   // Persistent blocks, one per CU: each runs work units (fetch_unit) until all queues are
   // empty.  Blocks are dispatched round-robin over the XCDs.
   const int xcd = blockIdx.x % kXcds;
-  __shared__ int s_unit;
+  // The next unit, broadcast by wave 0; it shares wave 0's staging area, which is idle from
+  // the end of one unit's epilogue to the next unit's epilogue.
+  int& s_unit = *reinterpret_cast<int*>(smem + RINGB);
   auto run_item = [&](const int unit) __attribute__((always_inline)) {
   const int h = unit / p.n_items;
   const Item it = p.items[unit - h * p.n_items];
@@ -227,8 +231,11 @@ void attn_kernel(AttnParams p) {
                  uint32_t((((wave * 64 + lane) % CH) ^ swz<D>(dma_row0)) * 16);
   auto make_rsrc = [&](const uint16_t* t) __attribute__((always_inline)) -> i32x4 {
     const uint64_t a = reinterpret_cast<uint64_t>(t) + uint64_t(h) * (D * 2);
-    return i32x4{int32_t(uint32_t(a)), int32_t(uint32_t(a >> 32) & 0xFFFF),
-                 int32_t(p.tensor_bytes - uint32_t(h) * (D * 2)), kBufferWord3};
+    // readfirstlane: the descriptor is uniform, and the buffer loads need it in SGPRs even
+    // where the compiler cannot prove that through the unit loop's control flow
+    return i32x4{__builtin_amdgcn_readfirstlane(int32_t(uint32_t(a))),
+                 __builtin_amdgcn_readfirstlane(int32_t(uint32_t(a >> 32) & 0xFFFF)),
+                 __builtin_amdgcn_readfirstlane(int32_t(p.tensor_bytes - uint32_t(h) * (D * 2))), kBufferWord3};
   };
   const i32x4 rsrc_k = make_rsrc(p.k), rsrc_v = make_rsrc(p.v);
 
@@ -647,55 +654,84 @@ void attn_kernel(AttnParams p) {
 #undef WA_WAIT_VMCNT
 
   if (!wave_active) return;
+  // ---- Output.  A lane holds 4-column pieces of its row spread over the row, so direct
+  // stores would write 32 rows per instruction in 8- or 16-byte pieces.  Each 32-row block
+  // goes through this wave's LDS staging area instead (16-byte chunks XOR-swizzled by row)
+  // and leaves as whole rows: 16 lanes x 16 bytes per 256 bytes of a row.
+  unsigned char* const stage = smem + RINGB + wave * STAGEB;
+  const bool partial = it.split >= 0;
+  // Lane indices redefined here (empty asm) so that the staging addresses, which depend only
+  // on them, are computed here and not hoisted out of the unit loop into the tile loop's
+  // register budget.
+  int orow_l = l32, olane = lane;
+  asm volatile("" : "+v"(orow_l), "+v"(olane));
+  constexpr int EB = OUT_F32 ? 4 : 2;  // bytes per element of the final output
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int qrow = row0 + 32 * qb + l32;
     const float l_tot = [&] {
       const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, l_run[qb]),
                                                       __builtin_bit_cast(uint32_t, l_run[qb]), false, false);
       return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
     }();
-    if (qrow >= it.q_end) continue;
-    if (it.split < 0) {
-      const float inv = 1.f / l_tot;
-      if constexpr (OUT_F32) {
-        float* orow = reinterpret_cast<float*>(p.out) + ((int64_t)qrow * H + h) * D;
+    const int rows_here = it.q_end - (row0 + 32 * qb);  // valid rows of this block (may be <= 0)
+    if (rows_here <= 0) continue;
+    auto emit = [&](auto eb_c, auto row_dst) __attribute__((always_inline)) {
+      constexpr int E = decltype(eb_c)::value;       // bytes per element
+      constexpr int RB = D * E;                      // bytes per output row
+      constexpr int CR = (RB < 256 ? RB : 256) / 16;  // 16-byte chunks per row per round
+      constexpr int ROUNDS = RB / (CR * 16);
+      static_assert(32 * CR * 16 <= STAGEB, "one round of 32 rows fits the staging area");
+      const float mul = 1.f / l_tot;
+#pragma unroll
+      for (int rd = 0; rd < ROUNDS; ++rd) {
+        // write: the lane's 4-element pieces of row l32 that fall in this round
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const int dv = 32 * db + 8 * g4 + 4 * hh;
-            const f32x4 o = {oacc[qb][db][4 * g4] * inv, oacc[qb][db][4 * g4 + 1] * inv,
-                             oacc[qb][db][4 * g4 + 2] * inv, oacc[qb][db][4 * g4 + 3] * inv};
-            *reinterpret_cast<f32x4*>(orow + dv) = o;
+            const int off = (32 * db + 8 * g4) * E + (E == 2 ? 8 : 16) * hh - rd * CR * 16;  // byte offset in the round
+            if (off < 0 || off >= CR * 16) continue;
+            const int c = off >> 4, within = off & 15;
+            unsigned char* dst = stage + orow_l * (CR * 16) + ((c ^ (orow_l & (CR - 1))) << 4) + within;
+            const float v0 = oacc[qb][db][4 * g4] * mul, v1 = oacc[qb][db][4 * g4 + 1] * mul;
+            const float v2 = oacc[qb][db][4 * g4 + 2] * mul, v3 = oacc[qb][db][4 * g4 + 3] * mul;
+            if constexpr (E == 2) {
+              *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            } else {
+              *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+            }
           }
-      } else {
-        uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + ((int64_t)qrow * H + h) * D;
+        // read back whole chunks in row order and store them
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dv = 32 * db + 8 * g4 + 4 * hh;
-            const u32x2 o = {pack_bf16x2(oacc[qb][db][4 * g4] * inv, oacc[qb][db][4 * g4 + 1] * inv),
-                             pack_bf16x2(oacc[qb][db][4 * g4 + 2] * inv, oacc[qb][db][4 * g4 + 3] * inv)};
-            *reinterpret_cast<u32x2*>(orow + dv) = o;
-          }
-      }
-    } else {
-      const int64_t slot = ((int64_t)it.split * p.G + (qrow - p.frame_rows)) * H + h;
-      float* po = p.part_o + slot * D;
-#pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int dv = 32 * db + 8 * g4 + 4 * hh;
-          const f32x4 o = {oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
-                           oacc[qb][db][4 * g4 + 3]};
-          *reinterpret_cast<f32x4*>(po + dv) = o;
+        for (int k = 0; k < 32 * CR / 64; ++k) {
+          const int j = k * 64 + olane, r = j / CR, c = j % CR;
+          const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (CR * 16) + ((c ^ (r & (CR - 1))) << 4));
+          if (r < rows_here) *reinterpret_cast<u32x4*>(row_dst(row0 + 32 * qb + r) + rd * CR * 16 + c * 16) = x;
         }
-      if (hh == 0) {
-        const float2 ml = make_float2(m_run[qb] * c2, l_tot);
-        *reinterpret_cast<float2*>(p.part_ml + slot * 2) = ml;
+      }
+    };
+    if (!partial) {
+      emit(std::integral_constant<int, EB>{}, [&](int qrow) __attribute__((always_inline)) {
+        return reinterpret_cast<unsigned char*>(p.out) + ((int64_t)qrow * H + h) * D * EB;
+      });
+    } else {
+      const int qrow = row0 + 32 * qb + l32;
+      if (qrow < it.q_end) {
+        const int64_t slot = ((int64_t)it.split * p.G + (qrow - p.frame_rows)) * H + h;
+        float* po = p.part_o + slot * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dv = 32 * db + 8 * g4 + 4 * hh;
+            const f32x4 o = {oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
+                             oacc[qb][db][4 * g4 + 3]};
+            *reinterpret_cast<f32x4*>(po + dv) = o;
+          }
+        if (hh == 0) {
+          const float2 ml = make_float2(m_run[qb] * c2, l_tot);
+          *reinterpret_cast<float2*>(p.part_ml + slot * 2) = ml;
+        }
       }
     }
   }
