@@ -39,7 +39,8 @@
 //   The running max is raised lazily: exponentials are taken against the running max,
 //   and a wave-uniform slow path raises it (rescaling the accumulators) only when some
 //   row's max grew by more than 2^8 (values up to 2^8 are exact in the softmax ratio);
-//   the same path masks keys past a segment end.
+//   the same path masks keys past a segment end.  Whether a tile needs it for reasons other
+//   than its data (first tile, masked keys) is known before the tile: one scalar compare.
 //   The launch is persistent: one block per CU takes work units from its XCD's queue in the
 //   plan's launch order (blocks are dispatched round-robin over the XCDs), a contiguous run
 //   of window units, so the query tiles of one group run side by side and share that XCD's
@@ -160,16 +161,13 @@ constexpr int32_t kBufferWord3 = 0x00020000;
 // One block = 4 waves (one per SIMD); one wave = 64 query rows as two 32-row blocks
 // (qb = 0, 1).  Every K and V fragment read from LDS feeds both blocks' matrix ops.
 //
-// Per 64-key tile the wave runs four phases; each pairs matrix ops with independent
-// vector work so that the matrix pipe stays busy (ALU work issues while a matrix op runs):
-//   P1  S0 = K Q0^T
-//   P2  S1 = K Q1^T                 | softmax(S0) -> P0, transpose reads of the V tile
-//   P3  O0 += V^T P0^T              | softmax(S1) -> P1
-//   --  wait for the next tile's DMA, barrier, DMA of the tile after it into this buffer
-//   P4  O1 += V^T P1^T              | K fragment reads of the next tile, row sums of P0, P1
-// The exponentials of a tile are taken against the running max before the tile's own max
-// is known; a wave-uniform slow path redoes a query block when that max exceeds the
-// running one by more than 2^8 or when the tile has masked keys (segment end).
+// Per 64-key tile the wave runs four slots of matrix ops (S of block 0, PV of block 1 for
+// the previous tile, S of block 1, PV of block 0), each paired with vector work of the
+// other block that does not depend on them, so the matrix pipe stays busy (the software
+// pipeline is laid out before the tile loop).  The exponentials of a tile are taken
+// against the running max before the tile's own max is known; a wave-uniform slow path
+// redoes a block's tile when some weight exceeds 2^8, and for a unit's first tile and
+// tiles with masked keys (segment end, causal diagonal).
 template <int D, bool OUT_F32>
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attn_kernel(AttnParams p) {
@@ -181,8 +179,8 @@ void attn_kernel(AttnParams p) {
   constexpr int KS = D / 16;                    // MFMA k-steps over d
   constexpr int DB = D / 32;                    // 32-wide output column blocks
   static_assert(NJ % kNW == 0, "tile slices must divide evenly over the waves");
-  constexpr float kLazyLog2 = 8.f;              // rescale only when the max grows by > 2^8
-  constexpr float kRowSumLimit = 256.f;         // fast path only while this lane's row sum <= 2^8
+  constexpr float kLazyLog2 = 8.f;              // slow path: rescale only when the max grows by > 2^8
+  constexpr float kRowSumLimit = 256.f;         // fast path only while every P of the tile <= 2^8
 
   constexpr int NBUF = 4;                       // LDS ring of (K, V) tile pairs
   constexpr int RINGB = NBUF * 2 * TILEB;       // bytes of the ring
@@ -237,7 +235,12 @@ void attn_kernel(AttnParams p) {
                  __builtin_amdgcn_readfirstlane(int32_t(uint32_t(a >> 32) & 0xFFFF)),
                  __builtin_amdgcn_readfirstlane(int32_t(p.tensor_bytes - uint32_t(h) * (D * 2))), kBufferWord3};
   };
-  const i32x4 rsrc_k = make_rsrc(p.k), rsrc_v = make_rsrc(p.v);
+  i32x4 rsrc_k = make_rsrc(p.k), rsrc_v = make_rsrc(p.v);
+  // A buffer load may read an SGPR that a vector instruction wrote (the readfirstlane above)
+  // only 5 wait states later.  The loads are inline asm, which the compiler's hazard checks
+  // do not see, so the wait is explicit, once per unit; from here on the descriptors are
+  // this asm's results, so nothing but scalar moves lies between them and the loads.
+  asm volatile("s_nop 4" : "+s"(rsrc_k), "+s"(rsrc_v));
 
   // ---- LDS read offsets (bytes within a tile)
   uint32_t koff[KS];  // K fragment (key row l32 of a 32-key block, chunk 2s+hh)
@@ -384,16 +387,39 @@ void attn_kernel(AttnParams p) {
     const f32x2 r = other_half(x);
     return __builtin_fmaxf(r[0], r[1]);
   };
-  // Keeps the fast-path P computed ahead of the slow-path branch (and so inside the phase
-  // whose matrix ops hide it): an empty asm that reads it.
-  auto pin_p = [&](int qb) __attribute__((always_inline)) {
-    asm volatile("" ::"v"(pw[qb][0]), "v"(pw[qb][1]), "v"(pw[qb][2]), "v"(pw[qb][3]), "v"(pw[qb][4]),
-                 "v"(pw[qb][5]), "v"(pw[qb][6]), "v"(pw[qb][7]), "v"(pw[qb][8]), "v"(pw[qb][9]), "v"(pw[qb][10]),
-                 "v"(pw[qb][11]), "v"(pw[qb][12]), "v"(pw[qb][13]), "v"(pw[qb][14]), "v"(pw[qb][15]));
-  };
-  // Slow path of one query block (wave-uniform): mask keys past the segment end, raise the
-  // running max (rescaling the accumulators) when it grew by more than 2^8, redo P and its
-  // row sums.
+  // ---- Software pipeline over 64-key tiles, one "slot" = one group of matrix ops with a
+  // share of the vector work that is independent of them:
+  //   slot 0: S0(t) = K(t) Q0^T          | P1(t-1) pairs 8..15, 2nd half of the DMA of t+2;
+  //                                        then the slow path of block 1 (tile t-1) if due
+  //   slot 1: O1 += V(t-1)^T P1(t-1)^T   | P0(t) pairs 0..7, row sums of P1(t-1), V(t)
+  //                                        transpose reads (each fragment right after its
+  //                                        last use by this slot)
+  //   slot 2: S1(t) = K(t) Q1^T          | P0(t) pairs 8..15; then the slow path of block 0
+  //                                        (tile t) if due
+  //   barrier: tile t+1 has landed for every wave
+  //   slot 3: O0 += V(t)^T P0(t)^T       | P1(t) pairs 0..7, K(t+1) reads, row sums of P0(t),
+  //                                        1st half of the DMA of t+3
+  // The LDS ring has 4 slots: the DMA of t+3 overwrites tile t-1, whose reads every wave
+  // finished before the barrier of tile t.  Before the first tile, block 1's "previous tile"
+  // is empty (scores -inf, V zero), so every iteration runs the same code; block 1's last
+  // PV runs after the loop.
+  // P pairs are staged: pair k's FMAs issue at step fs(k), its exponentials one step later,
+  // its bf16 packing and its row sums in the next steps (see stage_at); beside the S
+  // matrix ops the packing waits two steps, since an op that reads a fresh exp2 result one
+  // matrix op later stalls there.
+  // Each stage's result is pinned at its step (an empty asm that reads it): without the
+  // pins the compiler sinks pure arithmetic next to its first use, which puts dependent
+  // vector ops back to back.
+  // Slow path.  The exponentials are taken against the running max as it stands; a block's
+  // tile goes to the slow path (wave-uniform), which finds the tile max and raises the
+  // running max when it grew by more than 2^8, when
+  //   - it is the unit's first tile or has masked keys (segment end, causal diagonal): known
+  //     before the tile, one scalar compare per tile;
+  //   - some row sum of the tile exceeds 2^8 (any P above 2^8 makes it so).
+  constexpr int NS = 2 * KS;                // matrix ops of an S slot
+  constexpr int NP = 4 * DB;                // matrix ops of a PV slot
+  static_assert(NS % 4 == 0 && NP % 4 == 0 && (2 * KS) % NP == 0 && 16 % NP == 0 && NLD % 2 == 0,
+                "slot work must divide evenly over the steps");
   auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0) __attribute__((always_inline)) {
     if (valid < kBN || causal) {
       // tile keys at or past `lim` are masked: the segment end, and for causal items also
@@ -429,35 +455,6 @@ void attn_kernel(AttnParams p) {
     for (int n = 0; n < 16; ++n) p_pair(qb, sa, n, mc[qb]);
   };
 
-  // ---- Software pipeline over 64-key tiles, one "slot" = one group of matrix ops with a
-  // share of the vector work that is independent of them:
-  //   slot 0: S0(t) = K(t) Q0^T          | P1(t-1) pairs 8..15, 2nd half of the DMA of t+2;
-  //                                        then the check of block 1 (tile t-1)
-  //   slot 1: O1 += V(t-1)^T P1(t-1)^T   | P0(t) pairs 0..7, row sums of P1(t-1), V(t)
-  //                                        transpose reads (each fragment right after its
-  //                                        last use by this slot)
-  //   slot 2: S1(t) = K(t) Q1^T          | P0(t) pairs 8..15; then the check of block 0
-  //   barrier: tile t+1 has landed for every wave
-  //   slot 3: O0 += V(t)^T P0(t)^T       | P1(t) pairs 0..7, K(t+1) reads, row sums of P0(t),
-  //                                        1st half of the DMA of t+3
-  // The LDS ring has 4 slots: the DMA of t+3 overwrites tile t-1, whose reads every wave
-  // finished before the barrier of tile t.  Before the first tile, block 1's "previous tile"
-  // is empty (scores -inf, V zero), so every iteration runs the same code; block 1's last
-  // PV runs after the loop.
-  // P pairs are staged: pair k's FMAs issue at step fs(k), its exponentials one step later,
-  // its bf16 packing and its row sums in the next steps (see stage_at); beside the S
-  // matrix ops the packing waits two steps, since an op that reads a fresh exp2 result one
-  // matrix op later stalls there.
-  // Each stage's result is pinned at its step (an empty asm that reads it): without the
-  // pins the compiler sinks pure arithmetic next to its first use, which puts dependent
-  // vector ops back to back.
-  // The fast path needs no tile max: any P above 2^8 (a score more than 2^8 above the
-  // running max, in exp2 units) makes this lane's row sum exceed 2^8, and that (or the first
-  // tile, or a masked tile) sends the block to the slow path, which finds the max.
-  constexpr int NS = 2 * KS;                // matrix ops of an S slot
-  constexpr int NP = 4 * DB;                // matrix ops of a PV slot
-  static_assert(NS % 4 == 0 && NP % 4 == 0 && (2 * KS) % NP == 0 && 16 % NP == 0 && NLD % 2 == 0,
-                "slot work must divide evenly over the steps");
   f32x16 s0[2], s1[2];
 #pragma unroll
   for (int b = 0; b < 2; ++b)
@@ -504,20 +501,42 @@ void attn_kernel(AttnParams p) {
       }
     }
   };
-  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool first) __attribute__((always_inline)) {
+  // Keeps the fast-path P computed ahead of the slow-path branch (and so inside the slot
+  // whose matrix ops hide it): an empty asm that reads it.
+  auto pin_p = [&](int qb) __attribute__((always_inline)) {
+    asm volatile("" ::"v"(pw[qb][0]), "v"(pw[qb][1]), "v"(pw[qb][2]), "v"(pw[qb][3]), "v"(pw[qb][4]),
+                 "v"(pw[qb][5]), "v"(pw[qb][6]), "v"(pw[qb][7]), "v"(pw[qb][8]), "v"(pw[qb][9]), "v"(pw[qb][10]),
+                 "v"(pw[qb][11]), "v"(pw[qb][12]), "v"(pw[qb][13]), "v"(pw[qb][14]), "v"(pw[qb][15]));
+  };
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool dirty) __attribute__((always_inline)) {
     pin_p(qb);
     asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
-    if (first || valid < kBN || (causal && n0 + kBN - 1 > row0 + 32 * qb) ||
-        __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
-      slow_block(qb, sa, valid, n0);
+    if (dirty || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0) slow_block(qb, sa, valid, n0);
     l_run[qb] += rs[qb][0] + rs[qb][1];
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Tiles that take the slow path whatever their data (see above), as "the next such tile
+  // after u": the first tile, the last tile of a segment that ends inside it, and for causal
+  // items every tile from the first one with a key after some row of the wave (all tiles when
+  // forced).  Block 1 checks each tile one iteration after block 0 and reuses its verdict
+  // (block 0's causal rows come first, so this is conservative for block 1).
+  const int t_rag0 = (it.kv0_end - it.kv0_begin) % kBN != 0 ? nt0 - 1 : -1;
+  const int t_rag1 = nt1 > 0 && (it.kv1_end - it.kv1_begin) % kBN != 0 ? nt - 1 : -1;
+  const int t_all = !causal ? nt : [&] {
+    const int x = row0 - (kBN - 1) - it.kv0_begin;  // tile t is masked for row0 iff t * kBN > x
+    return x < 0 ? 0 : x / kBN + 1;
+  }();
+  auto next_dirty = [&](int u) __attribute__((always_inline)) -> int {
+    int n = u + 1 > t_all ? u + 1 : t_all;
+    if (t_rag0 > u && t_rag0 < n) n = t_rag0;
+    if (t_rag1 > u && t_rag1 < n) n = t_rag1;
+    return n;
+  };
+  // PV slot of block qb: N matrix ops (when `mma`), then the tail steps for the staged pairs.
   // Steps after the last matrix op of a slot in which the staged pairs finish: the last pair
   // starts at step 7 * N / 8 and ends at most 4 steps later (N = NS = NP).
   static_assert(NS == NP, "S and PV slots have the same number of steps");
   constexpr int kTail = 7 * NS / 8 + 5 - NS;
-  // PV slot of block qb: N matrix ops (when `mma`), then the tail steps for the staged pairs.
   auto pv_slot = [&](int qb, bool mma, auto&& extra) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < NP + kTail; ++i) {
@@ -588,20 +607,24 @@ void attn_kernel(AttnParams p) {
   for (int db = 0; db < DB; ++db) voff[db][0] += TILEB, voff[db][1] += TILEB;
 
   int valid_prev = kBN, n0_prev = 0;
+  int nd = 0;                // next tile that takes the slow path
+  bool dirty_prev = false;   // block 0's verdict on the previous tile (tile -1: none)
   for (int t = 0; t < nt; ++t) {
     const uint32_t step_k = ring(t + 2) - ring(t + 1);  // slot advance after this tile's reads
     const uint32_t step_v = ring(t + 1) - ring(t);
     int n0, nend;
     tile_range(t, n0, nend);
     const int valid = nend - n0;
+    const bool dirty = t == nd;
+    if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
 
-    if (wave_active) {
+    if (__builtin_expect(wave_active, 1)) {
       // slot 0
       s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
         stage_at(1, s1, 8, NS, i);
         if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)), toff_a);
       });
-      check_block(1, s1, valid_prev, n0_prev, t == 1);
+      check_block(1, s1, valid_prev, n0_prev, dirty_prev);
       // slot 1
       rs[0][0] = rs[0][1] = 0.f;
       pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
@@ -615,7 +638,7 @@ void attn_kernel(AttnParams p) {
       for (int db = 0; db < DB; ++db) voff[db][0] += step_v, voff[db][1] += step_v;
       // slot 2
       s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
-      check_block(0, s0, valid, n0, t == 0);
+      check_block(0, s0, valid, n0, dirty);
     } else {
 #pragma unroll
       for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx, toff_a);
@@ -625,7 +648,7 @@ void attn_kernel(AttnParams p) {
     barrier();           // ... for every wave
     toff_a = tile_off(t + 3);
 
-    if (wave_active) {
+    if (__builtin_expect(wave_active, 1)) {
       // slot 3 (after the last tile the K reads hit a buffer nobody uses)
       rs[1][0] = rs[1][1] = 0.f;
       pv_slot(0, true, [&](int i) __attribute__((always_inline)) {
@@ -644,11 +667,12 @@ void attn_kernel(AttnParams p) {
     }
     valid_prev = valid;
     n0_prev = n0;
+    dirty_prev = dirty;
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no DMA may still write this block's LDS at exit
   if (wave_active) {  // block 1 of the last tile
     s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { stage_at(1, s1, 8, NS, i); });
-    check_block(1, s1, valid_prev, n0_prev, nt == 1);
+    check_block(1, s1, valid_prev, n0_prev, dirty_prev);
     pv_slot(1, true, [&](int) __attribute__((always_inline)) {});
   }
 #undef WA_WAIT_VMCNT

@@ -159,6 +159,55 @@ def test_rows_sum_to_one_and_fp32_output(gpu_lib):
     assert (out - 1).abs().max().item() <= 4e-3
 
 
+def _hot_key(q, k, row, key, factor):
+    """Make key `key` of every head the direction of q[row] scaled by `factor`, so that
+    row `row` scores it about factor * |q|^2 / sqrt(d) (hundreds here): far above anything
+    earlier in the row, beyond what exponentials against a stale running max can hold."""
+    k[key] = (q[row].float() * factor).to(k.dtype)
+
+
+def test_score_jump_parity(gpu_lib):
+    """Scores that jump far above the running max after a unit's first tile, in window
+    rows and in global rows (the split global leg): exponentials against the stale max
+    would overflow, so the per-tile test must send those tiles to the slow path."""
+    T, S, G, K, r, H, d = 4, 256, 64, 1, 3, 2, 128
+    _say(f"score jump T={T} S={S} G={G} K={K} r={r} H={H} d={d}")
+    L = T * S + G
+    q, k, v = make_custom_inputs(L, H, d, torch.bfloat16, seed=9)
+    _hot_key(q, k, 5, 900, 10.0)         # window row, key in a late tile of its unit
+    _hot_key(q, k, T * S + 10, 700, 10.0)  # global row
+    _hot_key(q, k, 300, 1030, 12.0)      # window row, hot key among the global keys
+    plan = gpu_lib.wa_plan_create(T, S, G, K, r, H, d)
+    out = gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    ref = window_attention_reference(q, k, v, Geometry(T, S, G, K, r))
+    got = out.float().cpu()
+    rel, mx = _errors(got, ref)
+    _say(f"rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert not torch.isnan(got).any()
+    assert rel <= REL_L2 and mx <= MAX_ABS
+    # the hot rows are (almost) one-hot on their key
+    for row, key in ((5, 900), (T * S + 10, 700), (300, 1030)):
+        assert np.abs(got[row].numpy() - v[key].float().numpy()).max() <= 2e-2, row
+
+
+def test_score_jump_causal(gpu_lib):
+    # bf16 inputs: products of exactly representable values, so scores in the hundreds
+    # carry no input-rounding error (fp32 inputs would be rounded to bf16 first, and an
+    # error of a fraction of a unit in such scores moves the softmax weights visibly)
+    n, H, d = 1000, 1, 64
+    _say(f"score jump causal n={n} H={H} d={d}")
+    q, k, v = make_custom_inputs(n, H, d, torch.bfloat16, seed=10)
+    _hot_key(q, k, 900, 500, 12.0)  # key 500: a fast-path tile of row 900's item
+    plan = gpu_lib.wa_causal_plan_create(n, H, d)
+    out = gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda())
+    torch.cuda.synchronize()
+    ref = causal_attention_reference(q, k, v)
+    rel, mx = _errors(out.float().cpu(), ref)
+    _say(f"causal score jump: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert rel <= REL_L2 and mx <= MAX_ABS
+
+
 # ---------------------------------------------------------------- causal (audio VAE)
 
 
