@@ -108,6 +108,8 @@ def test_h3_scale_sampled_parity(gpu_lib, name):
     ((9, 33, 130, 2, 3), 2, 128, torch.bfloat16),  # radius >= chunks with globals; 2 global tiles
     ((11, 70, 65, 3, 1), 1, 128, torch.bfloat16),  # rows not a multiple of 32/64/128
     ((40, 48, 200, 1, 2), 2, 64, torch.bfloat16),  # K = 1, many groups, split global leg
+    ((6, 300, 40, 1, 1), 2, 128, torch.bfloat16),  # 44-row window and 40-row global items
+    ((7, 60, 33, 1, 2), 3, 64, torch.float32),     # every item one wave (60-row chunks)
 ])
 def test_edge_geometries(gpu_lib, geom, H, d, dtype):
     T, S, G, K, r = geom
