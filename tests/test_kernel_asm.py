@@ -35,10 +35,13 @@ def _sgpr_hazards(lines, window=8):
     instruction wrote fewer than 5 wait states before it (within one basic block)."""
     found = []
     for i, line in enumerate(lines):
-        m = re.search(r"buffer_load_dwordx4 \w+, s\[(\d+):(\d+)\]", line)
+        m = re.search(r"buffer_load_dwordx4 \w+, s\[(\d+):(\d+)\], (\w+)", line)
         if not m:
             continue
         regs = set(range(int(m.group(1)), int(m.group(2)) + 1))
+        so = re.match(r"s(\d+)$", m.group(3))  # the scalar offset, when it is a register
+        if so:
+            regs.add(int(so.group(1)))
         waits, seen, j = 0, 0, i - 1
         while j >= 0 and seen < window and waits < 5:
             t = lines[j].strip()
@@ -80,3 +83,6 @@ def test_hazard_scan_finds_a_planted_case():
     assert len(_sgpr_hazards(lines)) == 1
     lines[2] = "\ts_nop 4"
     assert _sgpr_hazards(lines) == []
+    # the scalar offset register is checked too
+    lines = ["\tv_readlane_b32 s12, v255, 3", "\ts_nop 0", "\tbuffer_load_dwordx4 v0, s[44:47], s12 offen lds"]
+    assert len(_sgpr_hazards(lines)) == 1
