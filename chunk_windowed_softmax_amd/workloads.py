@@ -114,3 +114,27 @@ def make_custom_inputs(L: int, H: int, d: int, dtype: torch.dtype, seed: int = 0
     if device != "cpu":
         q, k, v = (x.to(device) for x in (q, k, v))
     return q, k, v
+
+
+def make_rope_tables(L: int, d: int, base: float = 10000.0, device: str = "cpu"):
+    """Angle tables cos, sin [L, d/2] (fp32) for the QK-norm + rotary prologue: row t's
+    angle for channel pair j is t * base^(-2j/d), the common one-dimensional frequency
+    ladder, with the row index as position (a synthetic stand-in: the pages give no
+    positions or frequencies)."""
+    pos = torch.arange(L, dtype=torch.float64)[:, None]
+    freq = base ** (-2.0 * torch.arange(d // 2, dtype=torch.float64) / d)
+    ang = pos * freq[None, :]
+    cos, sin = torch.cos(ang).float(), torch.sin(ang).float()
+    if device != "cpu":
+        cos, sin = cos.to(device), sin.to(device)
+    return cos, sin
+
+
+def make_norm_weights(d: int, seed: int = 0, device: str = "cpu"):
+    """Per-channel RMSNorm weights (wq, wk) [d] fp32: 1 + 0.1 * randn (seeded)."""
+    g = torch.Generator("cpu").manual_seed(seed + 1000)
+    wq = 1.0 + 0.1 * torch.randn(d, generator=g)
+    wk = 1.0 + 0.1 * torch.randn(d, generator=g)
+    if device != "cpu":
+        wq, wk = wq.to(device), wk.to(device)
+    return wq, wk

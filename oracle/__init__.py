@@ -24,3 +24,8 @@ from .causal_attention import (  # noqa: F401
     causal_mask,
     causal_pairs_per_head,
 )
+from .qk_norm_rope import (  # noqa: F401
+    qk_norm_rope_reference,
+    rms_norm,
+    rope,
+)
