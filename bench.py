@@ -7,6 +7,10 @@ G=1024 global tokens, 7 heads of d=128, bf16), plus the fraction of MI355X's den
 MFMA peak.  One "step" is one wa_forward call (both legs and the merge) over inputs
 already resident in HBM.
 
+``--op prologue`` instead times the fused QK-RMSNorm + rotary prologue
+(wa_qk_norm_rope) on the same workload's q and k: a memory-bound pass, reported as
+algorithmic HBM GB/s against MI355X's 8 TB/s.
+
 Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on one GPU.
 """
 
@@ -30,8 +34,11 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="h3",
                     help="workload name (h3, h3_full, small, ragged, dense, audio_causal, audio_causal_small)")
+    ap.add_argument("--op", default="attention", choices=["attention", "prologue"],
+                    help="attention: wa_forward (default); prologue: wa_qk_norm_rope")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows the CPU oracle runs for --op prologue (0: all)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain device copy of q (known bytes) to calibrate HBM byte counters")
     return ap.parse_args()
@@ -78,19 +85,133 @@ def cpu_baseline(w, q, k, v, heads: int) -> dict:
     }
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch of the attention kernel from the committed rocprofv3 counters
-    (profiles/attn_kernel_<workload>.json), or None when absent or taken on other source."""
+def recorded_traffic(workload: str, kernel: str = "attn_kernel"):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counters
+    (profiles/<kernel>_<workload>.json), or None when absent or taken on other source."""
     from chunk_windowed_softmax_amd.rocprof_summary import kernel_source_sha256
 
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"attn_kernel_{workload}.json")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", f"{kernel}_{workload}.json")
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+    if rec.get("kernel_source_sha256") != kernel_source_sha256(kernel):
         return None, rec
     return rec["traffic_bytes"], rec
+
+
+def _time_calls(fn, steps: int, warmup: int, stream):
+    """Warm up, then time `steps` calls: HIP events on the launch stream around each call
+    and the wall clock around all of them (synchronised on both sides)."""
+    import torch
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        starts[i].record(stream)
+        fn()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall * 1e3 / steps
+
+
+def _calibration_copy(x):
+    import torch
+
+    scratch = torch.empty_like(x)
+    for _ in range(3):
+        scratch.copy_(x)
+    torch.cuda.synchronize()
+    print(f"calibration copy: {x.numel() * x.element_size()} bytes read and written per copy", flush=True)
+
+
+def prologue_bytes(L: int, H: int, d: int, elem: int, weights: bool) -> int:
+    """Algorithmic HBM bytes of one QK-norm + rotary call: q and k read and written once,
+    the fp32 cos and sin tables [L, d/2] read once, the two fp32 weight vectors."""
+    return 4 * L * H * d * elem + 2 * L * (d // 2) * 4 + (2 * d * 4 if weights else 0)
+
+
+def bench_prologue(args, w) -> int:
+    import torch
+
+    import chunk_windowed_softmax_amd as wa
+    from chunk_windowed_softmax_amd.workloads import make_norm_weights, make_prologue_inputs, make_rope_tables
+
+    dev = torch.device("cuda:0")
+    q_cpu, k_cpu = make_prologue_inputs(w.L, w.H, w.d, w.dtype, seed=0)
+    cos_cpu, sin_cpu = make_rope_tables(w.L, w.d)
+    wq_cpu, wk_cpu = make_norm_weights(w.d, 0)
+    q, k, cos, sin, wq, wk = (x.to(dev) for x in (q_cpu, k_cpu, cos_cpu, sin_cpu, wq_cpu, wk_cpu))
+    q_out, k_out = torch.empty_like(q), torch.empty_like(k)
+    stream = torch.cuda.current_stream(dev)
+    if args.calibration_copy:
+        _calibration_copy(q)
+
+    def call():
+        wa.wa_qk_norm_rope(q, k, cos, sin, wq, wk, q_out=q_out, k_out=k_out, stream=stream)
+
+    per_call, ms_step = _time_calls(call, args.steps, args.warmup, stream)
+    elem = q.element_size()
+    nbytes = prologue_bytes(w.L, w.H, w.d, elem, True)
+    value = nbytes / (ms_step * 1e-3) / 1e9
+    achieved = nbytes / (statistics.fmean(per_call) * 1e-3) / 1e9
+    traffic, traffic_rec = recorded_traffic(w.name, "qk_norm_rope_kernel")
+    res = {
+        "metric": "QK-RMSNorm + rotary prologue algorithmic HBM GB/s at the H3-scale window call on 1 MI355X",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"qk_norm_rope on {w.name} q/k", "L": w.L, "H": w.H, "d": w.d, "weights": True,
+            "pairs": "rotate-half", "bytes_per_call": nbytes, "parallelism": "single GPU",
+        },
+        "ms_per_call": {"median": round(statistics.median(per_call), 5), "min": round(min(per_call), 5),
+                        "mean": round(statistics.fmean(per_call), 5)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "qk_norm_rope_kernel per wa_qk_norm_rope call, HIP events on the launch stream",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "algorithmic_bytes": int(nbytes),
+            "traffic_source": None if traffic_rec is None else
+            f"profiles/qk_norm_rope_kernel_{w.name}.md" + ("" if traffic is not None else " (stale: kernel changed)"),
+        },
+    }
+    if not args.no_cpu_baseline:
+        from oracle import qk_norm_rope_reference
+
+        n = min(args.cpu_rows, w.L) if args.cpu_rows > 0 else w.L
+        t0 = time.perf_counter()
+        qk_norm_rope_reference(q_cpu[:n], k_cpu[:n], cos_cpu[:n], sin_cpu[:n], wq_cpu, wk_cpu)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {
+            "value": round(prologue_bytes(n, w.H, w.d, elem, True) / dt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": _cpu_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle on the first {n} of {w.L} rows (all {w.H} heads, q and k), "
+                      f"{dt:.2f} s wall",
+            "seconds": round(dt, 3),
+        }
+    print(json.dumps(res), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -110,6 +231,8 @@ def main() -> int:
         return 1
     wa.load_library()
     w = WORKLOADS[args.workload]
+    if args.op == "prologue":
+        return bench_prologue(args, w)
     q_cpu, k_cpu, v_cpu = make_inputs(w, seed=0)
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (q_cpu, k_cpu, v_cpu))
@@ -127,31 +250,13 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     if args.calibration_copy:
         # one read + one write of q.numel()*2 bytes per copy; profiled beside the attention
-        scratch = torch.empty_like(q)
-        for _ in range(3):
-            scratch.copy_(q)
-        torch.cuda.synchronize()
-        print(f"calibration copy: {q.numel() * q.element_size()} bytes read and written per copy", flush=True)
-        del scratch
-    for _ in range(args.warmup):
-        wa.wa_forward(plan, q, k, v, out=out, stream=stream)
-    torch.cuda.synchronize()
+        _calibration_copy(q)
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        wa.wa_forward(plan, q, k, v, out=out, stream=stream)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    per_call = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    per_call, ms_step = _time_calls(lambda: wa.wa_forward(plan, q, k, v, out=out, stream=stream),
+                                    args.steps, args.warmup, stream)
     ms_med = statistics.median(per_call)
     ms_min = min(per_call)
     ms_mean = statistics.fmean(per_call)
-    ms_step = wall * 1e3 / args.steps
 
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (ms_mean * 1e-3) / 1e12

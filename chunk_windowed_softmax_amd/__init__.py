@@ -26,6 +26,7 @@ LIB_PATH = os.path.join(_PKG, "libwa.so")
 
 WA_OK, WA_ERR_INVALID, WA_ERR_UNSUPPORTED, WA_ERR_ALLOC, WA_ERR_HIP = range(5)
 WA_BF16, WA_F32 = 0, 1
+WA_ROPE_INTERLEAVED = 1
 WA_ITEM_COLS = 8
 
 # Every symbol include/wa.h declares.
@@ -39,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "wa_plan_kv_indices",
     "wa_plan_items",
     "wa_plan_launch_order",
+    "wa_qk_norm_rope",
     "wa_last_error",
 )
 
@@ -86,6 +88,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wa_plan_kv_indices.argtypes = [P, ctypes.c_int, i32p, ctypes.c_size_t]
     lib.wa_plan_items.argtypes = [P, i32p, ctypes.c_size_t]
     lib.wa_plan_launch_order.argtypes = [P, i32p, ctypes.c_size_t]
+    lib.wa_qk_norm_rope.argtypes = [P] * 8 + [ctypes.c_int] * 3 + [ctypes.c_float] + [ctypes.c_int] * 2 + [P]
     lib.wa_last_error.argtypes = []
     lib.wa_last_error.restype = ctypes.c_char_p
     for name in EXPORTED_SYMBOLS:
@@ -222,8 +225,52 @@ def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
     return out
 
 
+def wa_qk_norm_rope(q, k, cos, sin, wq=None, wk=None, eps: float = 1e-6, interleaved: bool = False,
+                    q_out=None, k_out=None, stream=None):
+    """RMSNorm of q and k, then the rotary embedding, in one launch; returns (q_out, k_out).
+
+    q, k: contiguous GPU tensors [L, H, d] (bfloat16 or float32, d = 64 or 128).
+    cos, sin: contiguous float32 GPU tensors [L, d/2].  wq, wk: float32 [d] or None.
+    q_out / k_out default to new tensors; passing q / k itself works in place.
+    """
+    import torch
+
+    if q.dim() != 3:
+        raise ValueError("q must be [L, H, d]")
+    L, H, d = q.shape
+    dtype = q.dtype
+    if dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"unsupported dtype {dtype}; use bfloat16 or float32")
+    if q_out is None:
+        q_out = torch.empty_like(q)
+    if k_out is None:
+        k_out = torch.empty_like(k)
+    for name, t in (("k", k), ("q_out", q_out), ("k_out", k_out)):
+        if tuple(t.shape) != (L, H, d) or t.dtype != dtype:
+            raise ValueError(f"{name} must have the shape and dtype of q")
+    for name, t in (("cos", cos), ("sin", sin)):
+        if tuple(t.shape) != (L, d // 2) or t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32 [L, d/2]")
+    for name, t in (("wq", wq), ("wk", wk)):
+        if t is not None and (tuple(t.shape) != (d,) or t.dtype != torch.float32):
+            raise ValueError(f"{name} must be float32 [d] or None")
+    tensors = [t for t in (q, k, q_out, k_out, cos, sin, wq, wk) if t is not None]
+    for t in tensors:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("every tensor must be a contiguous GPU tensor")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    ptr = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+    with torch.cuda.device(q.device):
+        _check(load_library().wa_qk_norm_rope(
+            ptr(q), ptr(k), ptr(q_out), ptr(k_out), ptr(cos), ptr(sin), ptr(wq), ptr(wk), L, H, d, eps,
+            WA_ROPE_INTERLEAVED if interleaved else 0, WA_F32 if dtype == torch.float32 else WA_BF16,
+            ctypes.c_void_p(stream.cuda_stream)))
+    return q_out, k_out
+
+
 __all__ = [
     "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
     "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
-    "wa_plan_launch_order", "wa_causal_plan_create",
+    "wa_plan_launch_order", "wa_causal_plan_create", "wa_qk_norm_rope", "WA_ROPE_INTERLEAVED",
 ]

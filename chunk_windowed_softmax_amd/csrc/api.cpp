@@ -330,6 +330,56 @@ int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v
   return WA_OK;
 }
 
+int wa_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* cos, const float* sin,
+                    const float* wq, const float* wk, int L, int H, int d, float eps, int flags, int dtype,
+                    void* stream_v) {
+  if (dtype != WA_BF16 && dtype != WA_F32) return fail(WA_ERR_INVALID, "wa_qk_norm_rope: dtype must be WA_BF16 or WA_F32");
+  if (flags & ~WA_ROPE_INTERLEAVED) return fail(WA_ERR_INVALID, "wa_qk_norm_rope: unknown flags");
+  if (L < 0 || H < 1) return fail(WA_ERR_INVALID, "wa_qk_norm_rope: need L >= 0 and H >= 1");
+  if (!(eps >= 0.f) || eps > 1e30f) return fail(WA_ERR_INVALID, "wa_qk_norm_rope: eps must be finite and >= 0");
+  if (d != 64 && d != 128) return fail(WA_ERR_UNSUPPORTED, "wa_qk_norm_rope: d must be 64 or 128");
+  if (int64_t(L) * H * d >= (int64_t(1) << 31))
+    return fail(WA_ERR_UNSUPPORTED, "wa_qk_norm_rope: L*H*d must be below 2^31");
+  if (L == 0) return WA_OK;  // nothing to touch: the pointers may be anything, NULL included
+  if (!q || !k || !q_out || !k_out || !cos || !sin)
+    return fail(WA_ERR_INVALID, "wa_qk_norm_rope: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_out) || !aligned16(k_out) || !aligned16(cos) ||
+      !aligned16(sin) || (wq && !aligned16(wq)) || (wk && !aligned16(wk)))
+    return fail(WA_ERR_INVALID, "wa_qk_norm_rope: pointers must be 16-byte aligned");
+  {
+    const size_t bytes = size_t(L) * H * d * (dtype == WA_F32 ? 4 : 2);
+    // each output may be its own input (in place) but must not touch any other tensor
+    const void* ins[2] = {q, k};
+    const void* outs[2] = {q_out, k_out};
+    for (int o = 0; o < 2; ++o)
+      for (int i = 0; i < 2; ++i)
+        if (o != i && overlaps(outs[o], ins[i], bytes))
+          return fail(WA_ERR_INVALID, "wa_qk_norm_rope: an output overlaps the other input");
+    if (overlaps(q_out, k_out, bytes)) return fail(WA_ERR_INVALID, "wa_qk_norm_rope: q_out overlaps k_out");
+    for (int o = 0; o < 2; ++o)
+      if (outs[o] != ins[o] && overlaps(outs[o], ins[o], bytes))
+        return fail(WA_ERR_INVALID, "wa_qk_norm_rope: an output partly overlaps its input");
+  }
+  wa::PrologueArgs a;
+  a.q = q;
+  a.k = k;
+  a.q_out = q_out;
+  a.k_out = k_out;
+  a.cos = cos;
+  a.sin = sin;
+  a.wq = wq;
+  a.wk = wk;
+  a.L = L;
+  a.H = H;
+  a.d = d;
+  a.eps = eps;
+  a.f32 = dtype == WA_F32;
+  a.interleaved = (flags & WA_ROPE_INTERLEAVED) != 0;
+  hipError_t e = wa::launch_qk_norm_rope(a, static_cast<hipStream_t>(stream_v));
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_qk_norm_rope launch: ") + hipGetErrorString(e));
+  return WA_OK;
+}
+
 const char* wa_last_error(void) { return g_last_error.c_str(); }
 
 }  // extern "C"

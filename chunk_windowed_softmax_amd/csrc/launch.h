@@ -37,4 +37,21 @@ hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 // Enqueue an fp32 -> bf16 (round to nearest even) conversion of n elements (n % 4 == 0).
 hipError_t launch_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_t stream);
 
+struct PrologueArgs {
+  const void* q;          // [L, H, d] bf16 or fp32 (f32)
+  const void* k;
+  void* q_out;            // same shape and type; may be q itself
+  void* k_out;
+  const float* cos;       // [L, d/2] fp32
+  const float* sin;
+  const float* wq;        // [d] fp32 or nullptr (affine-free)
+  const float* wk;
+  int L, H, d;
+  float eps;
+  bool f32, interleaved;
+};
+
+// Enqueue the QK-RMSNorm + rotary-embedding pass (q and k in one launch).
+hipError_t launch_qk_norm_rope(const PrologueArgs& a, hipStream_t stream);
+
 }  // namespace wa

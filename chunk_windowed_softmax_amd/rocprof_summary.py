@@ -4,9 +4,10 @@ Inputs (all CSV, written with ``rocprofv3 --output-format csv``):
 
 * a ``--kernel-trace --stats`` run: per-kernel call counts and durations;
 * a ``--pmc FETCH_SIZE`` run and a ``--pmc WRITE_SIZE`` run of ``bench.py --calibration-copy``:
-  both counters (KiB per dispatch) are read for the attention kernel and for the plain
+  both counters (KiB per dispatch) are read for the profiled kernel (``--kernel``: the
+  attention kernel by default, or the QK-norm + rotary prologue) and for the plain
   device copy of a known byte count that the calibration step runs first.  Each counter is
-  scaled by (known copy bytes / counter reading of the copy), so the attention kernel's
+  scaled by (known copy bytes / counter reading of the copy), so the kernel's
   HBM bytes are expressed in the units of a transfer whose size is known.
 
 Output: ``<out>.md`` (human summary with the commands) and ``<out>.json`` (figures that
@@ -31,14 +32,15 @@ import statistics
 from typing import Dict, List
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-KERNEL_SOURCE = os.path.join(PKG, "csrc", "kernels.hip")
 ATTN = "attn_kernel"
 COMBINE = "combine_kernel"
+PROLOGUE = "qk_norm_rope_kernel"
 COPY = "copyBuffer"
+SOURCES = {ATTN: "kernels.hip", PROLOGUE: "prologue.hip"}
 
 
-def kernel_source_sha256() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
+def kernel_source_sha256(kernel: str = ATTN) -> str:
+    with open(os.path.join(PKG, "csrc", SOURCES[kernel]), "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
 
 
@@ -51,7 +53,7 @@ def _rows(pattern: str) -> List[Dict[str, str]]:
 
 
 def _short(name: str) -> str:
-    for key in (ATTN, COMBINE, COPY):
+    for key in (ATTN, COMBINE, PROLOGUE, COPY):
         if key in name:
             return key
     return name[:60]
@@ -98,7 +100,8 @@ def main() -> int:
     ap.add_argument("--copy-bytes", type=int, required=True)
     ap.add_argument("--out", required=True)
     ap.add_argument("--workload", default="h3")
-    ap.add_argument("--flop-per-call", type=float, required=True)
+    ap.add_argument("--kernel", default=ATTN, choices=sorted(SOURCES))
+    ap.add_argument("--flop-per-call", type=float, default=0.0)
     ap.add_argument("--algorithmic-bytes", type=float, required=True)
     ap.add_argument("--command-trace", default="")
     ap.add_argument("--command-fetch", default="")
@@ -109,6 +112,7 @@ def main() -> int:
     ap.add_argument("--simds", type=int, default=1024)
     ap.add_argument("--cus", type=int, default=256)
     a = ap.parse_args()
+    kern = a.kernel  # the profiled kernel
 
     dur = trace_durations(a.trace)
     fetch = counter_means(a.fetch, "FETCH_SIZE")
@@ -116,19 +120,19 @@ def main() -> int:
     copy_kib = a.copy_bytes / 1024.0
     f_fetch = copy_kib / fetch[COPY]
     f_write = copy_kib / write[COPY]
-    attn_fetch = fetch[ATTN] * f_fetch * 1024.0
-    attn_write = write[ATTN] * f_write * 1024.0
-    attn_ns = statistics.fmean(dur[ATTN])
+    attn_fetch = fetch[kern] * f_fetch * 1024.0
+    attn_write = write[kern] * f_write * 1024.0
+    attn_ns = statistics.fmean(dur[kern])
     res = {
         "workload": a.workload,
-        "kernel": ATTN,
-        "kernel_source_sha256": kernel_source_sha256(),
+        "kernel": kern,
+        "kernel_source_sha256": kernel_source_sha256(kern),
         "avg_duration_ms": attn_ns / 1e6,
-        "median_duration_ms": statistics.median(dur[ATTN]) / 1e6,
-        "calls": len(dur[ATTN]),
-        "tflops_at_avg_duration": a.flop_per_call / (attn_ns * 1e-9) / 1e12,
-        "fetch_kib_raw": fetch[ATTN],
-        "write_kib_raw": write[ATTN],
+        "median_duration_ms": statistics.median(dur[kern]) / 1e6,
+        "calls": len(dur[kern]),
+        "tflops_at_avg_duration": a.flop_per_call / (attn_ns * 1e-9) / 1e12 if a.flop_per_call else None,
+        "fetch_kib_raw": fetch[kern],
+        "write_kib_raw": write[kern],
         "copy_scale_fetch": f_fetch,
         "copy_scale_write": f_write,
         "fetch_bytes": attn_fetch,
@@ -136,10 +140,11 @@ def main() -> int:
         "traffic_bytes": attn_fetch + attn_write,
         "algorithmic_bytes": a.algorithmic_bytes,
         "hbm_gbs_at_avg_duration": (attn_fetch + attn_write) / (attn_ns * 1e-9) / 1e9,
+        "algorithmic_gbs_at_avg_duration": a.algorithmic_bytes / (attn_ns * 1e-9) / 1e9,
     }
     sq_lines = []
     if a.sq:
-        sq = sq_means(a.sq)[ATTN]
+        sq = sq_means(a.sq)[kern]
         xcd_cycles = sq["GRBM_GUI_ACTIVE"] / a.xcds  # GPU cycles of one XCD over the dispatch
         clock_ghz = xcd_cycles / sq["_duration_ns"]
         mfma_busy = sq["SQ_VALU_MFMA_BUSY_CYCLES"] / (xcd_cycles * a.simds)
@@ -163,7 +168,7 @@ def main() -> int:
     with open(a.out + ".json", "w") as f:
         json.dump(res, f, indent=1)
     lines = [
-        f"# rocprofv3 summary: `{ATTN}` on the {a.workload} workload",
+        f"# rocprofv3 summary: `{kern}` on the {a.workload} workload",
         "",
         "Commands (run from the repository root on one MI355X):",
         "",
@@ -177,18 +182,21 @@ def main() -> int:
     for k, v in sorted(dur.items()):
         lines.append(f"| {k} | {len(v)} | {statistics.fmean(v)/1e6:.4f} | {statistics.median(v)/1e6:.4f} | "
                      f"{min(v)/1e6:.4f} | {max(v)/1e6:.4f} |")
+    if a.flop_per_call:
+        lines += ["", f"Kept-pair FLOP per call: {a.flop_per_call:.6g}; at the average `{kern}` duration: "
+                  f"{res['tflops_at_avg_duration']:.1f} TFLOP/s."]
     lines += [
         "",
-        f"Kept-pair FLOP per call: {a.flop_per_call:.6g}; at the average `{ATTN}` duration: "
-        f"{res['tflops_at_avg_duration']:.1f} TFLOP/s.",
+        f"Algorithmic bytes per call: {a.algorithmic_bytes:.6g}; at the average `{kern}` duration: "
+        f"{res['algorithmic_gbs_at_avg_duration']:.0f} GB/s.",
         "",
         "HBM counters (KiB per dispatch, mean over dispatches), scaled by a plain copy of "
         f"{a.copy_bytes} bytes:",
         "",
-        "| counter | copy raw | scale | attn raw | attn bytes |",
+        "| counter | copy raw | scale | kernel raw | kernel bytes |",
         "|---|---|---|---|---|",
-        f"| FETCH_SIZE | {fetch[COPY]:.1f} | {f_fetch:.4f} | {fetch[ATTN]:.1f} | {attn_fetch:.4g} |",
-        f"| WRITE_SIZE | {write[COPY]:.1f} | {f_write:.4f} | {write[ATTN]:.1f} | {attn_write:.4g} |",
+        f"| FETCH_SIZE | {fetch[COPY]:.1f} | {f_fetch:.4f} | {fetch[kern]:.1f} | {attn_fetch:.4g} |",
+        f"| WRITE_SIZE | {write[COPY]:.1f} | {f_write:.4f} | {write[kern]:.1f} | {attn_write:.4g} |",
         "",
         f"Traffic per launch {res['traffic_bytes']:.4g} B vs algorithmic {a.algorithmic_bytes:.4g} B "
         f"(ratio {res['traffic_bytes'] / a.algorithmic_bytes:.2f}); {res['hbm_gbs_at_avg_duration']:.0f} GB/s.",

@@ -138,3 +138,16 @@ def make_norm_weights(d: int, seed: int = 0, device: str = "cpu"):
     if device != "cpu":
         wq, wk = wq.to(device), wk.to(device)
     return wq, wk
+
+
+def make_prologue_inputs(L: int, H: int, d: int, dtype=torch.bfloat16, seed: int = 0, device: str = "cpu"):
+    """q, k [L, H, d] for the QK-norm + rotary prologue: standard normal channels, each
+    (row, head) vector scaled by 10^u with u uniform in [-2, 2] so the norm sees a spread
+    of magnitudes (projection outputs before the norm are not unit-scaled)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    out = []
+    for _ in range(2):
+        x = torch.randn(L, H, d, generator=g)
+        x *= 10.0 ** (4.0 * torch.rand(L, H, 1, generator=g) - 2.0)
+        out.append(x.to(dtype).to(device) if device != "cpu" else x.to(dtype))
+    return out[0], out[1]

@@ -180,6 +180,37 @@ int wa_plan_items(const wa_plan* plan, int32_t* dst, size_t n);
  */
 int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n);
 
+/* Flags of wa_qk_norm_rope. */
+#define WA_ROPE_INTERLEAVED 1 /* rotate channel pairs (2j, 2j+1) instead of (j, j + d/2) */
+
+/*
+ * wa_qk_norm_rope -- the step before the attention, fused and out of place: RMSNorm of q
+ * and k followed by the rotary position embedding, written as the attention's input.
+ * (The ViT attention of the prhub digest of sglang PR #34949 applies qk_norm and the
+ * rotary embedding to q and k before attending, with an affine-free RMSNorm among the
+ * forms its contract tests cover; sglang PR #43164, Modifications item 2, fuses the norm
+ * and RoPE into one out-of-place kernel that writes the attention's input.)
+ * For every row t < L, head h < H and tensor x in {q, k} with weight w = wq or wk:
+ *   y = x[t,h,:] / sqrt(mean_c x[t,h,c]^2 + eps) * w      (w = 1 when the pointer is NULL)
+ *   out[t,h,j]     = y[j] cos[t,j] - y[j+d/2] sin[t,j]    for j < d/2
+ *   out[t,h,j+d/2] = y[j+d/2] cos[t,j] + y[j] sin[t,j]
+ * or, with WA_ROPE_INTERLEAVED, the same rotation of pair (2j, 2j+1) by angle j.
+ * q, k, q_out, k_out: device pointers to [L, H, d] tensors (the wa_forward layout) of
+ * element type `dtype` (WA_BF16 or WA_F32), 16-byte aligned, caller-owned; q_out may be q
+ * and k_out may be k (in place), other overlaps are rejected.  cos, sin: device pointers
+ * to [L, d/2] fp32 angle tables (row t's cosines and sines), 16-byte aligned.  wq, wk:
+ * device pointers to d fp32 weights, 16-byte aligned, or NULL.  eps >= 0.  d is 64 or 128.
+ * Computed in fp32; outputs rounded to `dtype` (nearest even).  v is not involved.
+ * stream: a hipStream_t (NULL = default); the call enqueues one kernel and returns
+ * without synchronising; it allocates nothing.  L = 0 enqueues nothing and reads no pointer
+ * (NULL is accepted then: an empty tensor may have no storage).
+ * Errors: WA_ERR_INVALID (NULL / misaligned / overlapping pointers, bad dtype, flags,
+ * L, H or eps), WA_ERR_UNSUPPORTED (d, or L*H*d >= 2^31), WA_ERR_HIP (launch failure).
+ */
+int wa_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* cos,
+                    const float* sin, const float* wq, const float* wk, int L, int H, int d,
+                    float eps, int flags, int dtype, void* stream);
+
 /* wa_last_error -- message of the calling thread's last non-zero status ("" if none). */
 const char* wa_last_error(void);
 
