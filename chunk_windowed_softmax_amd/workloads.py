@@ -151,3 +151,29 @@ def make_prologue_inputs(L: int, H: int, d: int, dtype=torch.bfloat16, seed: int
         x *= 10.0 ** (4.0 * torch.rand(L, H, 1, generator=g) - 2.0)
         out.append(x.to(dtype).to(device) if device != "cpu" else x.to(dtype))
     return out[0], out[1]
+
+
+def quantize_e4m3(x: torch.Tensor):
+    """(codes, scale): per-tensor e4m3 quantisation of a float tensor, scale = amax / 448 (the
+    largest e4m3 magnitude), codes = x / scale rounded to e4m3 by torch, as uint8."""
+    scale = float(x.abs().max()) / 448.0
+    if scale == 0.0:
+        scale = 1.0
+    codes = (x.float() / scale).to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes, scale
+
+
+def make_fp8_inputs(w: Workload, seed: int = 0, device: str = "cpu"):
+    """e4m3 codes of the workload's q, k, v (the make_inputs recipe in fp32) and their
+    per-tensor scales: (q8, k8, v8, scale_q, scale_k, scale_v)."""
+    g = torch.Generator("cpu").manual_seed(seed)
+    shape = (w.L, w.H, w.d)
+    xs = [torch.randn(shape, generator=g) for _ in range(3)]
+    if w.scaled_row_frac > 0:
+        n = int(round(w.scaled_row_frac * w.L))
+        idx = torch.randperm(w.L, generator=g)[:n]
+        xs[0][idx] *= 8.0
+        xs[1][idx] *= 8.0
+    out = [quantize_e4m3(x) for x in xs]
+    codes = [c if device == "cpu" else c.to(device) for c, _ in out]
+    return codes[0], codes[1], codes[2], out[0][1], out[1][1], out[2][1]

@@ -29,3 +29,10 @@ from .qk_norm_rope import (  # noqa: F401
     rms_norm,
     rope,
 )
+from .fp8 import (  # noqa: F401
+    decode_e4m3,
+    fp8_causal_attention_reference,
+    fp8_causal_attention_rows,
+    fp8_window_attention_reference,
+    fp8_window_attention_rows,
+)
