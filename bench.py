@@ -7,6 +7,9 @@ G=1024 global tokens, 7 heads of d=128, bf16), plus the fraction of MI355X's den
 MFMA peak.  One "step" is one wa_forward call (both legs and the merge) over inputs
 already resident in HBM.
 
+``--op fp8`` times the FP8 (e4m3) variant, wa_forward_fp8, on the same workload quantised
+per tensor, against the fp8 dense MFMA peak.
+
 ``--op prologue`` instead times the fused QK-RMSNorm + rotary prologue
 (wa_qk_norm_rope) on the same workload's q and k: a memory-bound pass, reported as
 algorithmic HBM GB/s against MI355X's 8 TB/s.
@@ -24,6 +27,7 @@ import sys
 import time
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+MFMA_FP8_PEAK_TFLOPS = 5033.2   # twice the bf16 rate
 HBM_PEAK_GBS = 8000.0
 
 
@@ -34,8 +38,8 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="h3",
                     help="workload name (h3, h3_full, small, ragged, dense, audio_causal, audio_causal_small)")
-    ap.add_argument("--op", default="attention", choices=["attention", "prologue"],
-                    help="attention: wa_forward (default); prologue: wa_qk_norm_rope")
+    ap.add_argument("--op", default="attention", choices=["attention", "prologue", "fp8"],
+                    help="attention: wa_forward (default); prologue: wa_qk_norm_rope; fp8: wa_forward_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-heads", type=int, default=3, help="heads of the workload the CPU oracle runs")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows the CPU oracle runs for --op prologue (0: all)")
@@ -137,6 +141,74 @@ def prologue_bytes(L: int, H: int, d: int, elem: int, weights: bool) -> int:
     return 4 * L * H * d * elem + 2 * L * (d // 2) * 4 + (2 * d * 4 if weights else 0)
 
 
+def bench_fp8(args, w) -> int:
+    import torch
+
+    import chunk_windowed_softmax_amd as wa
+    from chunk_windowed_softmax_amd.workloads import make_fp8_inputs
+
+    dev = torch.device("cuda:0")
+    q8c, k8c, v8c, sq, sk, sv = make_fp8_inputs(w, seed=0)
+    q8, k8, v8 = (x.to(dev) for x in (q8c, k8c, v8c))
+    out = torch.empty(q8.shape, dtype=torch.bfloat16, device=dev)
+    t0 = time.perf_counter()
+    plan = wa.wa_causal_plan_create(w.L, w.H, w.d) if w.causal else wa.wa_plan_create(
+        w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    info = plan.info
+    flop = info["kept_pairs_per_head"] * w.H * 4 * w.d
+    stream = torch.cuda.current_stream(dev)
+    if args.calibration_copy:
+        _calibration_copy(q8)
+    per_call, ms_step = _time_calls(lambda: wa.wa_forward_fp8(plan, q8, k8, v8, sq, sk, sv, out=out, stream=stream),
+                                    args.steps, args.warmup, stream)
+    value = flop / (ms_step * 1e-3) / 1e12
+    achieved = flop / (statistics.fmean(per_call) * 1e-3) / 1e12
+    traffic, traffic_rec = recorded_traffic(w.name, "attn_fp8_kernel")
+    res = {
+        "metric": "kept-pair TFLOP/s of the FP8 (e4m3) window call at the H3-scale share on 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic",
+        "config": {
+            "workload": f"fp8 {w.name}", "T": w.T, "S": w.S, "G": w.G, "K": w.K, "radius": w.radius,
+            "H": w.H, "d": w.d, "L": w.L, "kept_pairs": info["kept_pairs_per_head"] * w.H,
+            "flop_per_call": flop, "scales": "per tensor", "parallelism": "single GPU",
+        },
+        "ms_per_call": {"median": round(statistics.median(per_call), 4), "min": round(min(per_call), 4),
+                        "mean": round(statistics.fmean(per_call), 4)},
+        "plan_create_ms": round(plan_ms, 3),
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_fp8_kernel (+ split merge) per wa_forward_fp8 call, HIP events on the launch stream",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_FP8_PEAK_TFLOPS, 4),
+            "traffic": None if traffic is None else int(traffic),
+            "algorithmic_bytes": int(3 * w.L * w.H * w.d + 2 * w.L * w.H * w.d + 2 * info["workspace_bytes"]),
+            "traffic_source": None if traffic_rec is None else
+            f"profiles/attn_fp8_kernel_{w.name}.md" + ("" if traffic is not None else " (stale: kernel changed)"),
+        },
+    }
+    if not args.no_cpu_baseline:
+        from oracle import decode_e4m3
+
+        vals = [torch.from_numpy(decode_e4m3(c) * s) for c, s in ((q8c, sq), (k8c, sk), (v8c, sv))]
+        res["cpu_baseline"] = cpu_baseline(w, *vals, args.cpu_heads)
+        res["cpu_baseline"]["sample"] += " (decoded fp8 inputs)"
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def bench_prologue(args, w) -> int:
     import torch
 
@@ -233,6 +305,8 @@ def main() -> int:
     w = WORKLOADS[args.workload]
     if args.op == "prologue":
         return bench_prologue(args, w)
+    if args.op == "fp8":
+        return bench_fp8(args, w)
     q_cpu, k_cpu, v_cpu = make_inputs(w, seed=0)
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (q_cpu, k_cpu, v_cpu))

@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = (
     "wa_plan_items",
     "wa_plan_launch_order",
     "wa_qk_norm_rope",
+    "wa_forward_fp8",
     "wa_last_error",
 )
 
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wa_plan_kv_indices.argtypes = [P, ctypes.c_int, i32p, ctypes.c_size_t]
     lib.wa_plan_items.argtypes = [P, i32p, ctypes.c_size_t]
     lib.wa_plan_launch_order.argtypes = [P, i32p, ctypes.c_size_t]
+    lib.wa_forward_fp8.argtypes = [P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P]
     lib.wa_qk_norm_rope.argtypes = [P] * 8 + [ctypes.c_int] * 3 + [ctypes.c_float] + [ctypes.c_int] * 2 + [P]
     lib.wa_last_error.argtypes = []
     lib.wa_last_error.restype = ctypes.c_char_p
@@ -225,6 +227,35 @@ def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
     return out
 
 
+def wa_forward_fp8(plan: Plan, q, k, v, scale_q: float, scale_k: float, scale_v: float, out=None, stream=None):
+    """FP8 window attention; returns ``out`` ([L, H, d] bfloat16).
+
+    q, k, v: contiguous GPU tensors [L, H, 128] of e4m3 codes (torch.float8_e4m3fn or
+    uint8); the scales are their per-tensor dequantisation factors.
+    """
+    import torch
+
+    info = plan.info
+    shape = (info["L"], info["H"], info["d"])
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, plan expects {shape}")
+        if t.dtype not in (torch.float8_e4m3fn, torch.uint8):
+            raise ValueError(f"{name} must hold e4m3 codes (float8_e4m3fn or uint8), got {t.dtype}")
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    if out is None:
+        out = torch.empty(shape, dtype=torch.bfloat16, device=q.device)
+    elif tuple(out.shape) != shape or out.dtype != torch.bfloat16 or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out must be a contiguous bfloat16 GPU tensor of the plan's shape")
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    with torch.cuda.device(q.device):
+        _check(load_library().wa_forward_fp8(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), scale_q, scale_k,
+                                             scale_v, out.data_ptr(), ctypes.c_void_p(stream.cuda_stream)))
+    return out
+
+
 def wa_qk_norm_rope(q, k, cos, sin, wq=None, wk=None, eps: float = 1e-6, interleaved: bool = False,
                     q_out=None, k_out=None, stream=None):
     """RMSNorm of q and k, then the rotary embedding, in one launch; returns (q_out, k_out).
@@ -272,5 +303,5 @@ def wa_qk_norm_rope(q, k, cos, sin, wq=None, wk=None, eps: float = 1e-6, interle
 __all__ = [
     "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
     "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
-    "wa_plan_launch_order", "wa_causal_plan_create", "wa_qk_norm_rope", "WA_ROPE_INTERLEAVED",
+    "wa_plan_launch_order", "wa_causal_plan_create", "wa_qk_norm_rope", "WA_ROPE_INTERLEAVED", "wa_forward_fp8",
 ]

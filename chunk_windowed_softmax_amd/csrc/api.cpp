@@ -330,6 +330,50 @@ int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v
   return WA_OK;
 }
 
+int wa_forward_fp8(const wa_plan* cplan, const void* q, const void* k, const void* v, float scale_q, float scale_k,
+                   float scale_v, void* out, void* stream_v) {
+  if (!cplan) return fail(WA_ERR_INVALID, "wa_forward_fp8: plan is NULL");
+  if (!q || !k || !v || !out) return fail(WA_ERR_INVALID, "wa_forward_fp8: NULL tensor pointer");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(WA_ERR_INVALID, "wa_forward_fp8: tensors must be 16-byte aligned");
+  const float sc[3] = {scale_q, scale_k, scale_v};
+  for (float s : sc)
+    if (!(s > 0.f) || s > 1e30f) return fail(WA_ERR_INVALID, "wa_forward_fp8: scales must be finite and > 0");
+  wa_plan* plan = const_cast<wa_plan*>(cplan);
+  const wa::HostPlan& h = plan->host;
+  if (h.geo.d != 128) return fail(WA_ERR_UNSUPPORTED, "wa_forward_fp8: head size must be 128");
+  const int64_t elems = int64_t(h.L) * h.geo.H * h.geo.d;
+  // out holds 2 bytes per element, the inputs 1
+  auto hits = [&](const void* in) {
+    const uintptr_t o = reinterpret_cast<uintptr_t>(out), i = reinterpret_cast<uintptr_t>(in);
+    return o < i + size_t(elems) && i < o + size_t(elems) * 2;
+  };
+  if (hits(q) || hits(k) || hits(v)) return fail(WA_ERR_INVALID, "wa_forward_fp8: out overlaps an input");
+  DeviceResources* r = nullptr;
+  int st = device_resources(plan, &r);
+  if (st != WA_OK) return st;
+  wa::Fp8Args a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.out = out;
+  a.items = r->items;
+  a.n_items = (int)h.items.size();
+  a.H = h.geo.H;
+  a.G = h.geo.G;
+  a.L = h.L;
+  a.d = h.geo.d;
+  a.frame_rows = h.n_frame_rows;
+  a.n_splits = h.n_splits;
+  a.part_o = r->part;
+  a.part_ml = r->part ? r->part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;
+  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(h.geo.d)) * double(scale_q) * double(scale_k));
+  a.scale_v = scale_v;
+  hipError_t e = wa::launch_forward_fp8(a, static_cast<hipStream_t>(stream_v));
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward_fp8 launch: ") + hipGetErrorString(e));
+  return WA_OK;
+}
+
 int wa_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* cos, const float* sin,
                     const float* wq, const float* wk, int L, int H, int d, float eps, int flags, int dtype,
                     void* stream_v) {

@@ -1,0 +1,302 @@
+// FP8 (e4m3) variant of the decomposed window attention (gfx950).
+//
+// Same work items and output contract as attn_kernel (window items over their chunk span and
+// the global rows; global-leg items write fp32 partials that combine_kernel merges), with q,
+// k and v given as OCP e4m3 codes plus one fp32 scale per tensor (value = code * scale).  The
+// lqnn.cn article's fastest H3 configurations run in FP8 (§四); it does not say which
+// operands of the attention do, so both products run on gfx950's fp8 matrix cores here:
+//   S^T = K Q^T      v_mfma_f32_32x32x64_f8f6f4, A = K rows from LDS, B = the wave's Q rows
+//                    held in registers; the head dimension (128) is two k-steps of 64;
+//   O^T += V^T P^T   same instruction, B = P^T rounded to e4m3 straight from the S^T
+//                    accumulators, A = V^T gathered from the row-major V tile with
+//                    ds_read_b64_tr_b8 (LDS transpose read), in the key order of P.
+// Both operands of one matrix op map lane half h, byte j to the same k index, so any
+// consistent key (or channel) order is correct; the order used makes P's bytes the S^T
+// accumulator elements in register order.
+// Softmax: online over 64-key tiles in the log2 domain with the exact running max (the
+// accumulators are rescaled only when some row's max grows); P <= 1 before rounding; the
+// row sum adds the fp32 P.  Output: O * scale_v / rowsum, rounded to bf16.
+//
+// Block = 8 waves (two per SIMD), 32 query rows each: the plan's 256-row items, one block per
+// item and head.  K/V tiles (64 keys x 128 bytes each) are double-buffered in LDS: each of
+// the 512 threads loads 16 bytes of K and of V of the next tile into registers while the
+// current tile is computed, then stores them to the other buffer; one barrier per tile.
+// Rows are stored with their 16-byte chunks swizzled by row, so that the K fragment reads
+// are free of bank conflicts.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.h"
+
+namespace wa {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kD = 128;             // head size = bytes per fp8 row
+constexpr int kBN = kBlockN;        // keys per tile
+constexpr int kWaves = 8;           // waves per block
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRows = 32 * kWaves;  // query rows per block
+static_assert(kRows == kBlockM, "one block runs one plan item");
+static_assert(kBN == 64, "a P^T operand covers one 64-key tile");
+constexpr int kTileB = kBN * kD;  // bytes of one K (or V) tile
+constexpr int kBufB = 2 * kTileB;  // K then V
+
+// 16-byte chunk c of key row r sits at physical chunk c ^ swz(r): 16 consecutive rows at one
+// logical chunk then cover all 64 banks (rows of 128 bytes, two per 256-byte bank line).
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int lds_off(int r, int col) { return r * kD + (((col >> 4) ^ swz(r)) << 4) + (col & 15); }
+
+// Key of byte j (0..31) of a P^T / V^T operand in lane half h: the S^T accumulator element
+// j % 16 of key block j / 16, i.e. key (j/16)*32 + ((j%16)/4)*8 + 4h + j%4.
+__device__ __forceinline__ int key_of(int h, int j) { return (j >> 4) * 32 + ((j & 15) >> 2) * 8 + 4 * h + (j & 3); }
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2 x = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
+__global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int unit = blockIdx.x;
+  const int head = unit / p.n_items;
+  const Item it = p.items[unit - head * p.n_items];
+  const int H = p.H;
+  const int64_t row_stride = int64_t(H) * kD;  // bytes between consecutive rows of q/k/v
+  const bool causal = (it.flags & kItemCausal) != 0;
+
+  const int nt0 = (it.kv0_end - it.kv0_begin + kBN - 1) / kBN;
+  const int nt1 = it.kv1_end > it.kv1_begin ? (it.kv1_end - it.kv1_begin + kBN - 1) / kBN : 0;
+  const int nt = nt0 + nt1;
+  auto tile_range = [&](int t, int& n0, int& nend) {
+    if (t < nt0) {
+      n0 = it.kv0_begin + t * kBN;
+      nend = it.kv0_end;
+    } else {
+      n0 = it.kv1_begin + (t - nt0) * kBN;
+      nend = it.kv1_end;
+    }
+  };
+
+  // this thread's 16-byte chunk of the K and V tiles: key row tr, chunk tc
+  static_assert(kThreads * 16 == kTileB, "one 16-byte chunk of K and of V per thread and tile");
+  const int tr = tid >> 3, tc = tid & 7;
+  const unsigned char* kg = static_cast<const unsigned char*>(p.k) + int64_t(head) * kD + tc * 16;
+  const unsigned char* vg = static_cast<const unsigned char*>(p.v) + int64_t(head) * kD + tc * 16;
+  auto load_tile = [&](int t, u32x4& kx, u32x4& vx) {
+    int n0, nend;
+    tile_range(t, n0, nend);
+    const int key = n0 + tr;  // rows past the segment end are masked; past the tensor, zero
+    kx = vx = u32x4{0u, 0u, 0u, 0u};
+    if (key < p.L) {
+      kx = *reinterpret_cast<const u32x4*>(kg + int64_t(key) * row_stride);
+      vx = *reinterpret_cast<const u32x4*>(vg + int64_t(key) * row_stride);
+    }
+  };
+  auto store_tile = [&](int buf, const u32x4& kx, const u32x4& vx) {
+    unsigned char* b = smem + buf * kBufB;
+    *reinterpret_cast<u32x4*>(b + lds_off(tr, tc * 16)) = kx;
+    *reinterpret_cast<u32x4*>(b + kTileB + lds_off(tr, tc * 16)) = vx;
+  };
+
+  u32x4 kx, vx;
+  load_tile(0, kx, vx);
+
+  // Q fragments: lane = query row, bytes [64 s + 32 hh, +32) of the row for k-step s
+  const int qrow = it.q_begin + wave * 32 + l32;
+  const bool q_ok = qrow < it.q_end;
+  i32x8 qf[2];
+  {
+    const unsigned char* qg = static_cast<const unsigned char*>(p.q) + int64_t(qrow) * row_stride + int64_t(head) * kD;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+      if (q_ok) {
+        a = *reinterpret_cast<const u32x4*>(qg + 64 * s + 32 * hh);
+        b = *reinterpret_cast<const u32x4*>(qg + 64 * s + 32 * hh + 16);
+      }
+      qf[s] = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(b[0]), int(b[1]), int(b[2]), int(b[3])};
+    }
+  }
+  store_tile(0, kx, vx);
+  __syncthreads();
+
+  // V^T gather: transpose read m of lane (group g = lane / 16, index i = lane % 16) names
+  // key row key_of(hh, 8m + i/2) at column 16 (g & 1) + 8 (i & 1) of the d-block; the
+  // instruction hands lane i byte i % 8 of the rows named by lanes 2j + i / 8, j = 0..7.
+  const int gi = lane & 15, gsel = (lane >> 4) & 1;
+  int vrow[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) vrow[m] = key_of(hh, 8 * m + (gi >> 1));
+  const int vcol = 16 * gsel + 8 * (gi & 1);
+
+  const float c = p.scale_log2;  // log2(e) / sqrt(d) * scale_q * scale_k
+  float m_run = -__builtin_inff(), l_run = 0.f;
+  f32x16 oacc[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+
+  for (int t = 0; t < nt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nt) load_tile(t + 1, kx, vx);
+    const unsigned char* kb = smem + buf * kBufB;
+    const unsigned char* vb = kb + kTileB;
+    int n0, nend;
+    tile_range(t, n0, nend);
+    const int valid = nend - n0;
+
+    // S^T for the two 32-key blocks of the tile
+    f32x16 sa[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      sa[b] = f32x16{};
+      const int r = 32 * b + l32;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + lds_off(r, 64 * s + 32 * hh));
+        const u32x4 a2 = *reinterpret_cast<const u32x4*>(kb + lds_off(r, 64 * s + 32 * hh + 16));
+        const i32x8 kf = {int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(a2[0]), int(a2[1]), int(a2[2]), int(a2[3])};
+        sa[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[s], sa[b], 0, 0, 0, 0, 0, 0);
+      }
+    }
+    // mask keys past the segment end (and, for causal items, after the lane's own row)
+    const bool need_mask = valid < kBN || (causal && n0 + kBN - 1 > it.q_begin + wave * 32);
+    if (need_mask) {
+      int lim = valid;
+      if (causal) lim = __builtin_elementwise_min(lim, qrow - n0 + 1);
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (32 * b + (i >> 2) * 8 + 4 * hh + (i & 3) >= lim) sa[b][i] = -__builtin_inff();
+    }
+    // running max (log2 units); lanes l and l ^ 32 hold the two halves of one query's keys
+    float mt = sa[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
+    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+    const float m_new = __builtin_fmaxf(m_run, mt * c);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    // P = 2^(S c - m) <= 1, rounded to e4m3; byte j of the operand is element j % 16 of
+    // key block j / 16
+    const float mneg = m_run == -__builtin_inff() ? 0.f : -m_run;  // rows with no key yet: P = 0
+    i32x8 pb;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      const int b = w >> 2, e = 4 * (w & 3);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e], c, mneg));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 1], c, mneg));
+      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 2], c, mneg));
+      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 3], c, mneg));
+      l_run += (p0 + p1) + (p2 + p3);
+      int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+      x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+      pb[w] = x;
+    }
+    // O^T += V^T P^T per 32-row d-block
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      i32x8 vf;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (__attribute__((address_space(3))) i32x2*)(vb + lds_off(vrow[m], 32 * db + vcol)));
+        vf[2 * m] = x[0];
+        vf[2 * m + 1] = x[1];
+      }
+      oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pb, oacc[db], 0, 0, 0, 0, 0, 0);
+    }
+    if (t + 1 < nt) store_tile(buf ^ 1, kx, vx);
+    __syncthreads();
+  }
+
+  // ---- output: lane holds O^T[d][query] for d = 32 db + 8 (i / 4) + 4 hh + i % 4
+  const float l_tot = l_run + __shfl_xor(l_run, 32);
+  if (!q_ok) return;
+  if (it.split < 0) {
+    const float mul = p.scale_v / l_tot;
+    uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t(qrow) * H + head) * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * db + 8 * r + 4 * hh;
+        const u32x2 y = {pack_bf16x2(oacc[db][4 * r] * mul, oacc[db][4 * r + 1] * mul),
+                         pack_bf16x2(oacc[db][4 * r + 2] * mul, oacc[db][4 * r + 3] * mul)};
+        *reinterpret_cast<u32x2*>(o + d0) = y;
+      }
+  } else {
+    const int64_t slot = (int64_t(it.split) * p.G + (qrow - p.frame_rows)) * H + head;
+    float* po = p.part_o + slot * kD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d0 = 32 * db + 8 * r + 4 * hh;
+        *reinterpret_cast<float4*>(po + d0) =
+            make_float4(oacc[db][4 * r] * p.scale_v, oacc[db][4 * r + 1] * p.scale_v,
+                        oacc[db][4 * r + 2] * p.scale_v, oacc[db][4 * r + 3] * p.scale_v);
+      }
+    if (hh == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run, l_tot);
+  }
+}
+
+// Merge of the global leg's key splits (as for the bf16 path): for each (global row, head),
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s, in bf16.
+__global__ __launch_bounds__(64) void combine_fp8_kernel(const float* __restrict__ part_o,
+                                                         const float* __restrict__ part_ml, uint16_t* __restrict__ out,
+                                                         int G, int H, int n_splits, int frame_rows) {
+  const int gi = blockIdx.x / H, h = blockIdx.x % H;
+  const int64_t stride = int64_t(G) * H;
+  const int64_t slot0 = int64_t(gi) * H + h;
+  float M = -__builtin_inff();
+  for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_ml[(s * stride + slot0) * 2]);
+  float den = 0.f;
+  for (int s = 0; s < n_splits; ++s) {
+    const float* ml = part_ml + (s * stride + slot0) * 2;
+    den += __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+  }
+  const float inv = 1.f / den;
+  const int64_t orow = (int64_t(frame_rows + gi) * H + h) * kD;
+  for (int dv = threadIdx.x; dv < kD; dv += 64) {
+    float num = 0.f;
+    for (int s = 0; s < n_splits; ++s)
+      num += __builtin_amdgcn_exp2f(part_ml[(s * stride + slot0) * 2] - M) * part_o[(s * stride + slot0) * kD + dv];
+    const __bf16 b = (__bf16)(num * inv);
+    out[orow + dv] = __builtin_bit_cast(uint16_t, b);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream) {
+  if (a.d != kD) return hipErrorInvalidValue;
+  const int grid = a.H * a.n_items;
+  if (grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(kThreads), 2 * kBufB, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_splits <= 1) return e;
+  hipLaunchKernelGGL(combine_fp8_kernel, dim3(a.G * a.H), dim3(64), 0, stream, a.part_o, a.part_ml,
+                     static_cast<uint16_t*>(a.out), a.G, a.H, a.n_splits, a.frame_rows);
+  return hipGetLastError();
+}
+
+}  // namespace wa

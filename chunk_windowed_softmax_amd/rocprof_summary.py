@@ -35,8 +35,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ATTN = "attn_kernel"
 COMBINE = "combine_kernel"
 PROLOGUE = "qk_norm_rope_kernel"
+FP8 = "attn_fp8_kernel"
 COPY = "copyBuffer"
-SOURCES = {ATTN: "kernels.hip", PROLOGUE: "prologue.hip"}
+SOURCES = {ATTN: "kernels.hip", PROLOGUE: "prologue.hip", FP8: "attn_fp8.hip"}
 
 
 def kernel_source_sha256(kernel: str = ATTN) -> str:
@@ -53,7 +54,7 @@ def _rows(pattern: str) -> List[Dict[str, str]]:
 
 
 def _short(name: str) -> str:
-    for key in (ATTN, COMBINE, PROLOGUE, COPY):
+    for key in (ATTN, COMBINE, PROLOGUE, FP8, COPY):
         if key in name:
             return key
     return name[:60]

@@ -180,6 +180,28 @@ int wa_plan_items(const wa_plan* plan, int32_t* dst, size_t n);
  */
 int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n);
 
+/*
+ * wa_forward_fp8 -- the decomposed window attention of `plan` (any plan of wa_plan_create
+ * or wa_causal_plan_create with d = 128) on FP8 inputs.  (The lqnn.cn article on
+ * VDN-Minimax-H3 window attention quotes its fastest H3 configurations in FP8, §四; which
+ * operands of the attention run in FP8 is not stated there: here both matrix products do.)
+ * q, k, v: device pointers to [L, H, 128] OCP e4m3 (e4m3fn) codes, one byte each, 16-byte
+ * aligned, caller-owned; the value of a code is its e4m3 value times scale_q, scale_k or
+ * scale_v (finite, > 0).  out: device pointer to [L, H, 128] bf16, 16-byte aligned,
+ * overlapping no input.
+ * Computes out = softmax(scale_q scale_k q k^T / sqrt(d)) (scale_v v) over each row's kept
+ * keys, like wa_forward: scores and the softmax in fp32, the softmax weights rounded to e4m3
+ * for the second product (the one approximation beyond the inputs), the row sums over the
+ * fp32 weights, output rounded to bf16.
+ * stream: a hipStream_t (NULL = default).  Enqueues the kernels and returns without
+ * synchronising; shares the plan's workspace with wa_forward (calls on different streams
+ * that use one plan must be ordered by the caller).
+ * Errors: WA_ERR_INVALID (NULL plan or tensor, misalignment, overlap, bad scale),
+ * WA_ERR_UNSUPPORTED (d != 128), WA_ERR_ALLOC, WA_ERR_HIP.
+ */
+int wa_forward_fp8(const wa_plan* plan, const void* q, const void* k, const void* v, float scale_q,
+                   float scale_k, float scale_v, void* out, void* stream);
+
 /* Flags of wa_qk_norm_rope. */
 #define WA_ROPE_INTERLEAVED 1 /* rotate channel pairs (2j, 2j+1) instead of (j, j + d/2) */
 
