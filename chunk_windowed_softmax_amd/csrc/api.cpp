@@ -358,6 +358,8 @@ int wa_forward_fp8(const wa_plan* cplan, const void* q, const void* k, const voi
   a.v = v;
   a.out = out;
   a.items = r->items;
+  a.work = reinterpret_cast<const int32_t*>(r->items + h.items.size());
+  a.per_xcd = h.work_per_xcd;
   a.n_items = (int)h.items.size();
   a.H = h.geo.H;
   a.G = h.geo.G;

@@ -18,11 +18,11 @@
 // row sum adds the fp32 P.  Output: O * scale_v / rowsum, rounded to bf16.
 //
 // Block = 8 waves (two per SIMD), 32 query rows each: the plan's 256-row items, one block per
-// item and head.  K/V tiles (64 keys x 128 bytes each) are double-buffered in LDS: each of
+// item and head, in the plan's XCD-aware launch order.  K/V tiles (64 keys x 128 bytes each) are double-buffered in LDS: each of
 // the 512 threads loads 16 bytes of K and of V of the next tile into registers while the
 // current tile is computed, then stores them to the other buffer; one barrier per tile.
 // Rows are stored with their 16-byte chunks swizzled by row, so that the K fragment reads
-// are free of bank conflicts.
+// and the V transpose reads are free of bank conflicts.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -50,10 +50,19 @@ static_assert(kBN == 64, "a P^T operand covers one 64-key tile");
 constexpr int kTileB = kBN * kD;  // bytes of one K (or V) tile
 constexpr int kBufB = 2 * kTileB;  // K then V
 
-// 16-byte chunk c of key row r sits at physical chunk c ^ swz(r): 16 consecutive rows at one
-// logical chunk then cover all 64 banks (rows of 128 bytes, two per 256-byte bank line).
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int lds_off(int r, int col) { return r * kD + (((col >> 4) ^ swz(r)) << 4) + (col & 15); }
+// 16-byte chunk c of key row r sits at physical chunk c ^ swz(r) (rows of 128 bytes, two
+// per 256-byte bank line).
+//   K: swz = (r / 2) % 8, so the 16 consecutive rows of one ds_read_b128 pass at one logical
+//      chunk cover all 64 banks.
+//   V: swz = 2 * ((r / 2) % 2 + 2 * ((r / 8) % 2)).  One ds_read_b64_tr_b8 pass (32 lanes)
+//      reads 8 rows {B..B+3, B+8..B+11} (B a multiple of 4 with bits 1 and 3 clear) at the 4
+//      eight-byte pieces of two adjacent logical chunks; per row parity the 4 rows get 4
+//      distinct chunk pairs, so the pass covers all 64 banks.
+__device__ __forceinline__ int k_off(int r, int col) { return r * kD + (((col >> 4) ^ ((r >> 1) & 7)) << 4) + (col & 15); }
+__device__ __forceinline__ int v_off(int r, int col) {
+  const int sw = 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
+  return r * kD + (((col >> 4) ^ sw) << 4) + (col & 15);
+}
 
 // Key of byte j (0..31) of a P^T / V^T operand in lane half h: the S^T accumulator element
 // j % 16 of key block j / 16, i.e. key (j/16)*32 + ((j%16)/4)*8 + 4h + j%4.
@@ -68,7 +77,10 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int unit = blockIdx.x;
+  // the plan's launch order: blocks are dispatched round-robin over the XCDs, and each XCD's
+  // queue runs one group's query tiles side by side (they share its L2)
+  const int unit = p.work[int(blockIdx.x % kXcdCount) * p.per_xcd + int(blockIdx.x / kXcdCount)];
+  if (unit < 0) return;
   const int head = unit / p.n_items;
   const Item it = p.items[unit - head * p.n_items];
   const int H = p.H;
@@ -105,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
   };
   auto store_tile = [&](int buf, const u32x4& kx, const u32x4& vx) {
     unsigned char* b = smem + buf * kBufB;
-    *reinterpret_cast<u32x4*>(b + lds_off(tr, tc * 16)) = kx;
-    *reinterpret_cast<u32x4*>(b + kTileB + lds_off(tr, tc * 16)) = vx;
+    *reinterpret_cast<u32x4*>(b + k_off(tr, tc * 16)) = kx;
+    *reinterpret_cast<u32x4*>(b + kTileB + v_off(tr, tc * 16)) = vx;
   };
 
   u32x4 kx, vx;
@@ -163,8 +175,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
       const int r = 32 * b + l32;
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + lds_off(r, 64 * s + 32 * hh));
-        const u32x4 a2 = *reinterpret_cast<const u32x4*>(kb + lds_off(r, 64 * s + 32 * hh + 16));
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + k_off(r, 64 * s + 32 * hh));
+        const u32x4 a2 = *reinterpret_cast<const u32x4*>(kb + k_off(r, 64 * s + 32 * hh + 16));
         const i32x8 kf = {int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(a2[0]), int(a2[1]), int(a2[2]), int(a2[3])};
         sa[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[s], sa[b], 0, 0, 0, 0, 0, 0);
       }
@@ -186,7 +198,11 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
-    mt = __builtin_fmaxf(mt, __shfl_xor(mt, 32));
+    {  // lanes l and l ^ 32: one v_permlane32_swap
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt), __builtin_bit_cast(uint32_t, mt),
+                                                      false, false);
+      mt = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+    }
     const float m_new = __builtin_fmaxf(m_run, mt * c);
     if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
       const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
@@ -218,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (__attribute__((address_space(3))) i32x2*)(vb + lds_off(vrow[m], 32 * db + vcol)));
+            (__attribute__((address_space(3))) i32x2*)(vb + v_off(vrow[m], 32 * db + vcol)));
         vf[2 * m] = x[0];
         vf[2 * m + 1] = x[1];
       }
@@ -289,7 +305,7 @@ __global__ __launch_bounds__(64) void combine_fp8_kernel(const float* __restrict
 
 hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream) {
   if (a.d != kD) return hipErrorInvalidValue;
-  const int grid = a.H * a.n_items;
+  const int grid = kXcdCount * a.per_xcd;
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(kThreads), 2 * kBufB, stream, a);
   hipError_t e = hipGetLastError();

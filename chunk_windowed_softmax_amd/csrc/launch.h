@@ -60,6 +60,8 @@ struct Fp8Args {
   const void* v;
   void* out;              // bf16 [L, H, d]
   const Item* items;      // device copy of the plan's items
+  const int32_t* work;    // device copy of the launch order (kXcdCount * per_xcd units, -1 = none)
+  int per_xcd;
   int n_items, H, G, L, d, frame_rows, n_splits;
   float* part_o;          // [n_splits, G, H, d] fp32 (global-leg partials)
   float* part_ml;         // [n_splits, G, H, 2] fp32
