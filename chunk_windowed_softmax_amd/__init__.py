@@ -9,6 +9,8 @@ Functions carry the C names:
 * ``wa_plan_create(T, S, G, K, radius, H, d) -> Plan``
 * ``wa_causal_plan_create(n, H, d) -> Plan`` (causal dense attention, the audio VAE's)
 * ``wa_forward(plan, q, k, v, out=None) -> out``
+* ``wa_forward_fp8(plan, q8, k8, v8, scale_q, scale_k, scale_v, out=None) -> out`` (e4m3 inputs)
+* ``wa_qk_norm_rope(q, k, cos, sin, wq=None, wk=None, ...) -> (q_out, k_out)`` (the prologue)
 * ``wa_plan_info / wa_plan_groups / wa_plan_kv_indices / wa_plan_items / wa_plan_launch_order /
   wa_last_error``
 """
