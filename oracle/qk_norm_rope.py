@@ -11,7 +11,7 @@ Sources (web pages; cited by title and section):
   shape (batch, tokens, heads, head_dim), q and k go through ``qk_norm`` and the rotary
   position embedding (``rotary_pos_emb``, handed to ``forward``) before the attention; the
   digest's test list names a contract test for an affine-free RMSNorm as ``qk_norm``.
-* [Ulysses] sglang PR #43164 (MiniMax-H3 Ulysses exchange), Modifications item 2: one
+* [USP] sglang PR #43164 (MiniMax-H3 Ulysses exchange), Modifications item 2: one
   out-of-place kernel normalises q and k, applies RoPE and writes them (and v) to their
   destination, instead of an in-place norm followed by a copy.
 
