@@ -125,3 +125,29 @@ def test_fp8_rejects_other_head_sizes(gpu_lib):
     with pytest.raises(gpu_lib.WaError) as e:
         gpu_lib.wa_forward_fp8(plan, x, x, x, 1.0, 1.0, 1.0)
     assert e.value.code == 2
+
+
+@pytest.mark.parametrize("geom,H", [((6, 300, 40, 1, 1), 2), ((7, 60, 33, 1, 2), 3), ((3, 64, 0, 2, 1), 1)])
+def test_fp8_edge_geometries(gpu_lib, geom, H):
+    """Ragged chunks and frames, items of one wave or less, no global rows: full comparison."""
+    T, S, G, K, r = geom
+    L = T * S + G
+    g = torch.Generator().manual_seed(sum(geom) + H)
+    (q8, sq), (k8, sk), (v8, sv) = (quantize_e4m3(torch.randn(L, H, 128, generator=g)) for _ in range(3))
+    plan = gpu_lib.wa_plan_create(T, S, G, K, r, H, 128)
+    got = _run(gpu_lib, plan, q8, k8, v8, sq, sk, sv)
+    ref = fp8_window_attention_reference(q8, k8, v8, sq, sk, sv, Geometry(T, S, G, K, r))
+    _check(got, ref, np.nanmax(np.abs(decode_e4m3(v8))) * sv, f"edge {geom} H={H}")
+
+
+def test_fp8_covers_every_row_and_is_deterministic(gpu_lib):
+    """Every output element is written (NaN prefill), and two calls agree bit for bit."""
+    w = WORKLOADS["ragged"]
+    q8, k8, v8, sq, sk, sv = (x.cuda() if torch.is_tensor(x) else x for x in make_fp8_inputs(w, seed=6))
+    plan = _plan(gpu_lib, w)
+    out = torch.full((w.L, w.H, w.d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.wa_forward_fp8(plan, q8, k8, v8, sq, sk, sv, out=out)
+    again = gpu_lib.wa_forward_fp8(plan, q8, k8, v8, sq, sk, sv)
+    torch.cuda.synchronize()
+    assert not torch.isnan(out).any()
+    assert torch.equal(out, again)
