@@ -14,9 +14,9 @@
 // Both operands of one matrix op map lane half h, byte j to the same k index, so any
 // consistent key (or channel) order is correct; the order used makes P's bytes the S^T
 // accumulator elements in register order.
-// Softmax: online over 64-key tiles in the log2 domain with the exact running max (the
-// accumulators are rescaled only when some row's max grows); P <= 1 before rounding; the
-// row sum adds the fp32 P.  Output: O * scale_v / rowsum, rounded to bf16.
+// Softmax: online over the tiles in the log2 domain with a lazily raised running max (the
+// weights may reach 2^8 before it rises; see the loop); the row sum adds the fp32 weights.
+// Output: O * scale_v / rowsum, rounded to bf16.
 //
 // Block = 8 waves (two per SIMD), 32 query rows each: the plan's 256-row items, one block per
 // item and head, in the plan's XCD-aware launch order.  K/V tiles of 128 keys (16 KB each)
@@ -201,41 +201,52 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
         for (int i = 0; i < 16; ++i)
           if (32 * b + (i >> 2) * 8 + 4 * hh + (i & 3) >= lim) sa[b][i] = -__builtin_inff();
     }
-    // running max (log2 units); lanes l and l ^ 32 hold the two halves of one query's keys
-    float mt = sa[0][0];
+    // P = 2^(S c - m) against the running max m as it stands (lazy max): the weights may
+    // reach 2^8 (exact in e4m3, whose largest value is 448) before m must rise.  A tile
+    // whose row sum exceeds 2^8 (so possibly some weight too), and the first tile, take the
+    // wave-uniform slow path: tile max, raise m, rescale, recompute P.  Byte j of the P^T
+    // operand is element j % 16 of key block j / 16.
+    i32x8 pb[2];  // keys 0..63 and 64..127 of the tile
+    float l_tile = 0.f;
+    auto weights = [&](float mneg) __attribute__((always_inline)) {
+      l_tile = 0.f;
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+      for (int w = 0; w < 16; ++w) {
+        const int b = w >> 2, e = 4 * (w & 3);
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e], c, mneg));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 1], c, mneg));
+        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 2], c, mneg));
+        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 3], c, mneg));
+        l_tile += (p0 + p1) + (p2 + p3);
+        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
+        x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
+        pb[w >> 3][w & 7] = x;
+      }
+    };
+    bool slow = t == 0;
+    if (!slow) {
+      weights(-m_run);
+      slow = __builtin_amdgcn_ballot_w64(l_tile > 256.f) != 0;
+    }
+    if (slow) {
+      // tile max (log2 units); lanes l and l ^ 32 hold the two halves of one query's keys
+      float mt = sa[0][0];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
-    {  // lanes l and l ^ 32: one v_permlane32_swap
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
       const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt), __builtin_bit_cast(uint32_t, mt),
                                                       false, false);
       mt = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-    }
-    const float m_new = __builtin_fmaxf(m_run, mt * c);
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run) != 0) {
+      const float m_new = __builtin_fmaxf(m_run, mt * c);
       const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
       m_run = m_new;
+      weights(-m_run);
     }
-    // P = 2^(S c - m) <= 1, rounded to e4m3; byte j of the operand is element j % 16 of
-    // key block j / 16
-    const float mneg = m_run == -__builtin_inff() ? 0.f : -m_run;  // rows with no key yet: P = 0
-    i32x8 pb[2];  // keys 0..63 and 64..127 of the tile
-#pragma unroll
-    for (int w = 0; w < 16; ++w) {
-      const int b = w >> 2, e = 4 * (w & 3);
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e], c, mneg));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 1], c, mneg));
-      const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 2], c, mneg));
-      const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 3], c, mneg));
-      l_run += (p0 + p1) + (p2 + p3);
-      int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-      x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
-      pb[w >> 3][w & 7] = x;
-    }
+    l_run += l_tile;
     // O^T += V^T P^T per 32-row d-block
 #pragma unroll
     for (int db = 0; db < 4; ++db)
