@@ -20,10 +20,9 @@
 //
 // Block = 8 waves (two per SIMD), 32 query rows each: the plan's 256-row items, one block per
 // item and head, in the plan's XCD-aware launch order.  K/V tiles of 128 keys (16 KB each)
-// are double-buffered in LDS: each of the 512 threads loads 32 bytes of K and of V of the
-// next tile into registers while the current tile is computed, then stores them to the
-// other buffer; one barrier per tile (128-key tiles: 11% faster than 64-key ones, whose
-// barriers came twice as often).
+// are double-buffered in LDS and filled by direct global->LDS loads issued at the start of
+// the previous tile; one barrier per tile (128-key tiles: 11% faster than 64-key ones,
+// whose barriers came twice as often).
 // Rows are stored with their 16-byte chunks swizzled by row, so that the K fragment reads
 // and the V transpose reads are free of bank conflicts.
 #include <hip/hip_runtime.h>
@@ -61,6 +60,13 @@ constexpr int kBufB = 2 * kTileB;  // K then V
 //      reads 8 rows {B..B+3, B+8..B+11} (B a multiple of 4 with bits 1 and 3 clear) at the 4
 //      eight-byte pieces of two adjacent logical chunks; per row parity the 4 rows get 4
 //      distinct chunk pairs, so the pass covers all 64 banks.
+// s_waitcnt with vmcnt = 0 and the other counters left at their maximum.
+constexpr int kVmcnt0 = 0x0F70;
+// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle, so each
+// access of a lane is range checked against num_records (word 2) and reads 0 past it.
+constexpr int32_t kBufferWord3 = 0x00020000;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ int k_off(int r, int col) { return r * kD + (((col >> 4) ^ ((r >> 1) & 7)) << 4) + (col & 15); }
 __device__ __forceinline__ int v_off(int r, int col) {
   const int sw = 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
@@ -103,35 +109,49 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
     }
   };
 
-  // this thread's 16-byte chunk of the K and V tiles: key row tr, chunk tc
-  static_assert(kThreads * 32 == kTileB, "two 16-byte chunks of K and of V per thread and tile");
-  const int tr = tid >> 3, tc = tid & 7;  // rows tr and tr + 64
-  const unsigned char* kg = static_cast<const unsigned char*>(p.k) + int64_t(head) * kD + tc * 16;
-  const unsigned char* vg = static_cast<const unsigned char*>(p.v) + int64_t(head) * kD + tc * 16;
-  auto load_tile = [&](int t, u32x4 (&kx)[2], u32x4 (&vx)[2]) {
+  // K/V tiles go straight from global memory into LDS (buffer loads with the LDS bit: no
+  // registers, no LDS write instructions).  One load moves 64 lanes x 16 bytes into 1 KB of
+  // LDS (8 rows); wave w fills slices w and w + 8 of the K and of the V tile.  Lane l of
+  // slice s writes LDS chunk 64 s + l, i.e. row 8 s + l / 8 at physical chunk l % 8, which
+  // holds the row's logical chunk (l % 8) ^ swizzle(row): the swizzle is applied on the
+  // global side.  The buffer resources are based at this head's first byte and range checked
+  // against the end of the tensor (rows past it read as zero).
+  auto make_rsrc = [&](const void* t) __attribute__((always_inline)) -> i32x4 {
+    const uint64_t a = reinterpret_cast<uint64_t>(t) + uint64_t(head) * kD;
+    return i32x4{__builtin_amdgcn_readfirstlane(int32_t(uint32_t(a))),
+                 __builtin_amdgcn_readfirstlane(int32_t(uint32_t(a >> 32) & 0xFFFF)),
+                 __builtin_amdgcn_readfirstlane(int32_t(uint32_t(int64_t(p.L) * row_stride - int64_t(head) * kD))),
+                 kBufferWord3};
+  };
+  i32x4 rsrc_k = make_rsrc(p.k), rsrc_v = make_rsrc(p.v);
+  // a buffer load may read an SGPR written by a vector instruction (the readfirstlane) only
+  // 5 wait states later; the loads are inline asm, unseen by the compiler's hazard checks
+  asm volatile("s_nop 4" : "+s"(rsrc_k), "+s"(rsrc_v));
+  uint32_t dk[2], dv[2];  // byte offsets of the lane's 16 bytes within a tile (slices w, w + 8)
+#pragma unroll
+  for (int x = 0; x < 2; ++x) {
+    const int row = 8 * (wave + 8 * x) + (lane >> 3);
+    dk[x] = uint32_t(row) * uint32_t(row_stride) + uint32_t(((lane & 7) ^ ((row >> 1) & 7)) << 4);
+    dv[x] = uint32_t(row) * uint32_t(row_stride) +
+            uint32_t(((lane & 7) ^ (2 * (((row >> 1) & 1) | ((row >> 2) & 2)))) << 4);
+  }
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)smem));
+  auto dma_tile = [&](int t, int buf) __attribute__((always_inline)) {
     int n0, nend;
     tile_range(t, n0, nend);
+    const uint32_t toff = uint32_t(n0) * uint32_t(row_stride);
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
-      const int key = n0 + tr + 64 * x;  // rows past the segment end are masked; past the tensor, zero
-      kx[x] = vx[x] = u32x4{0u, 0u, 0u, 0u};
-      if (key < p.L) {
-        kx[x] = *reinterpret_cast<const u32x4*>(kg + int64_t(key) * row_stride);
-        vx[x] = *reinterpret_cast<const u32x4*>(vg + int64_t(key) * row_stride);
-      }
-    }
-  };
-  auto store_tile = [&](int buf, const u32x4 (&kx)[2], const u32x4 (&vx)[2]) {
-    unsigned char* b = smem + buf * kBufB;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      *reinterpret_cast<u32x4*>(b + k_off(tr + 64 * x, tc * 16)) = kx[x];
-      *reinterpret_cast<u32x4*>(b + kTileB + v_off(tr + 64 * x, tc * 16)) = vx[x];
+      const uint32_t lk = lds_base + uint32_t(buf * kBufB + (wave + 8 * x) * 1024);
+      const uint32_t lv = lk + kTileB;
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(dk[x] + toff), "s"(rsrc_k), "{m0}"(lk)
+                   : "memory");
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(dv[x] + toff), "s"(rsrc_v), "{m0}"(lv)
+                   : "memory");
     }
   };
 
-  u32x4 kx[2], vx[2];
-  load_tile(0, kx, vx);
+  dma_tile(0, 0);
 
   // Q fragments: lane = query row, bytes [64 s + 32 hh, +32) of the row for k-step s
   const int qrow = it.q_begin + wave * 32 + l32;
@@ -149,8 +169,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
       qf[s] = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(b[0]), int(b[1]), int(b[2]), int(b[3])};
     }
   }
-  store_tile(0, kx, vx);
-  __syncthreads();
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // tile 0 (and Q) have landed ...
+  __syncthreads();                       // ... for every wave
 
   // V^T gather: transpose read m of lane (group g = lane / 16, index i = lane % 16) names
   // key row key_of(hh, 8m + i/2) at column 16 (g & 1) + 8 (i & 1) of the d-block; the
@@ -169,7 +189,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
 
   for (int t = 0; t < nt; ++t) {
     const int buf = t & 1;
-    if (t + 1 < nt) load_tile(t + 1, kx, vx);
+    if (t + 1 < nt) dma_tile(t + 1, buf ^ 1);
     const unsigned char* kb = smem + buf * kBufB;
     const unsigned char* vb = kb + kTileB;
     int n0, nend;
@@ -262,8 +282,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
         }
         oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pb[hf], oacc[db], 0, 0, 0, 0, 0, 0);
       }
-    if (t + 1 < nt) store_tile(buf ^ 1, kx, vx);
-    __syncthreads();
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // tile t + 1 has landed ...
+    __syncthreads();                       // ... for every wave
   }
 
   // ---- output: lane holds O^T[d][query] for d = 32 db + 8 (i / 4) + 4 hh + i % 4

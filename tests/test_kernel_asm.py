@@ -20,12 +20,12 @@ CSRC = os.path.join(ROOT, "chunk_windowed_softmax_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def _compile_asm(tmp_path):
-    out = tmp_path / "kernels.s"
+def _compile_asm(tmp_path, source="kernels.hip"):
+    out = tmp_path / (source + ".s")
     cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fno-honor-nans",
            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
-           os.path.join(CSRC, "kernels.hip"), "-o", str(out), "-I", os.path.join(ROOT, "include"), "-I", CSRC]
+           os.path.join(CSRC, source), "-o", str(out), "-I", os.path.join(ROOT, "include"), "-I", CSRC]
     subprocess.run(cmd, check=True, capture_output=True, timeout=600)
     return out.read_text().split("\n")
 
@@ -70,8 +70,9 @@ def _sgpr_hazards(lines, window=8):
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
-def test_no_valu_sgpr_hazard_before_tile_loads(tmp_path):
-    lines = _compile_asm(tmp_path)
+@pytest.mark.parametrize("source", ["kernels.hip", "attn_fp8.hip"])
+def test_no_valu_sgpr_hazard_before_tile_loads(tmp_path, source):
+    lines = _compile_asm(tmp_path, source)
     loads = [l for l in lines if "buffer_load_dwordx4" in l and " lds" in l]
     assert loads, "no tile loads found in the compiled kernels"
     assert _sgpr_hazards(lines) == []
