@@ -1,7 +1,7 @@
 // FP8 (e4m3) variant of the decomposed window attention (gfx950).
 //
 // Same work items and output contract as attn_kernel (window items over their chunk span and
-// the global rows; global-leg items write fp32 partials that combine_kernel merges), with q,
+// the global rows; global-leg items write fp32 partials that a combine pass merges), with q,
 // k and v given as OCP e4m3 codes plus one fp32 scale per tensor (value = code * scale).  The
 // lqnn.cn article's fastest H3 configurations run in FP8 (§四); it does not say which
 // operands of the attention do, so both products run on gfx950's fp8 matrix cores here:
@@ -52,6 +52,13 @@ static_assert(kBN == 128, "a tile is two 64-key P^T operands");
 constexpr int kTileB = kBN * kD;  // bytes of one K (or V) tile
 constexpr int kBufB = 2 * kTileB;  // K then V
 
+// s_waitcnt with vmcnt = 0 and the other counters left at their maximum.
+constexpr int kVmcnt0 = 0x0F70;
+// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle, so each
+// access of a lane is range checked against num_records (word 2) and reads 0 past it.
+constexpr int32_t kBufferWord3 = 0x00020000;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 // 16-byte chunk c of key row r sits at physical chunk c ^ swz(r) (rows of 128 bytes, two
 // per 256-byte bank line).
 //   K: swz = (r / 2) % 8, so the 16 consecutive rows of one ds_read_b128 pass at one logical
@@ -60,13 +67,6 @@ constexpr int kBufB = 2 * kTileB;  // K then V
 //      reads 8 rows {B..B+3, B+8..B+11} (B a multiple of 4 with bits 1 and 3 clear) at the 4
 //      eight-byte pieces of two adjacent logical chunks; per row parity the 4 rows get 4
 //      distinct chunk pairs, so the pass covers all 64 banks.
-// s_waitcnt with vmcnt = 0 and the other counters left at their maximum.
-constexpr int kVmcnt0 = 0x0F70;
-// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle, so each
-// access of a lane is range checked against num_records (word 2) and reads 0 past it.
-constexpr int32_t kBufferWord3 = 0x00020000;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ int k_off(int r, int col) { return r * kD + (((col >> 4) ^ ((r >> 1) & 7)) << 4) + (col & 15); }
 __device__ __forceinline__ int v_off(int r, int col) {
   const int sw = 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
