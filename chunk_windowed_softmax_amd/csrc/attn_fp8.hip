@@ -18,11 +18,13 @@
 // weights may reach 2^8 before it rises; see the loop); the row sum adds the fp32 weights.
 // Output: O * scale_v / rowsum, rounded to bf16.
 //
-// Block = 8 waves (two per SIMD), 32 query rows each: the plan's 256-row items, one block per
-// item and head, in the plan's XCD-aware launch order.  K/V tiles of 128 keys (16 KB each)
-// are double-buffered in LDS and filled by direct global->LDS loads issued at the start of
-// the previous tile; one barrier per tile (128-key tiles: 11% faster than 64-key ones,
-// whose barriers came twice as often).
+// Block = 4 waves of 32 query rows, half of one of the plan's 256-row items; two blocks per
+// CU (two waves per SIMD from different blocks, whose phases drift apart: 2.4% faster than
+// one 8-wave block per item).  Blocks follow the plan's XCD-aware launch order, the two
+// halves of an item on one XCD.  K/V tiles of 128 keys (16 KB each) are double-buffered in
+// LDS and filled by direct global->LDS loads issued at the start of the previous tile; one
+// barrier per tile (128-key tiles: 11% faster than 64-key ones, whose barriers came twice as
+// often).
 // Rows are stored with their 16-byte chunks swizzled by row, so that the K fragment reads
 // and the V transpose reads are free of bank conflicts.
 #include <hip/hip_runtime.h>
@@ -44,10 +46,11 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kD = 128;             // head size = bytes per fp8 row
 constexpr int kBN = 2 * kBlockN;    // keys per tile
-constexpr int kWaves = 8;           // waves per block
+constexpr int kWaves = 4;           // waves per block (two blocks per CU)
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRows = 32 * kWaves;  // query rows per block
-static_assert(kRows == kBlockM, "one block runs one plan item");
+constexpr int kHalves = kBlockM / kRows;  // blocks per plan item
+static_assert(kHalves * kRows == kBlockM, "blocks split a plan item evenly");
 static_assert(kBN == 128, "a tile is two 64-key P^T operands");
 constexpr int kTileB = kBN * kD;  // bytes of one K (or V) tile
 constexpr int kBufB = 2 * kTileB;  // K then V
@@ -82,13 +85,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-__global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
+__global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(Fp8Args p) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hh = lane >> 5;
   // the plan's launch order: blocks are dispatched round-robin over the XCDs, and each XCD's
   // queue runs one group's query tiles side by side (they share its L2)
-  const int unit = p.work[int(blockIdx.x % kXcdCount) * p.per_xcd + int(blockIdx.x / kXcdCount)];
+  const int slot = int(blockIdx.x / kXcdCount);
+  const int unit = p.work[int(blockIdx.x % kXcdCount) * p.per_xcd + slot / kHalves];
+  const int part = slot % kHalves;  // this block's rows of the item
   if (unit < 0) return;
   const int head = unit / p.n_items;
   const Item it = p.items[unit - head * p.n_items];
@@ -111,10 +116,10 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
 
   // K/V tiles go straight from global memory into LDS (buffer loads with the LDS bit: no
   // registers, no LDS write instructions).  One load moves 64 lanes x 16 bytes into 1 KB of
-  // LDS (8 rows); wave w fills slices w and w + 8 of the K and of the V tile.  Lane l of
-  // slice s writes LDS chunk 64 s + l, i.e. row 8 s + l / 8 at physical chunk l % 8, which
-  // holds the row's logical chunk (l % 8) ^ swizzle(row): the swizzle is applied on the
-  // global side.  The buffer resources are based at this head's first byte and range checked
+  // LDS (8 rows); wave w fills slices w, w + 4, w + 8 and w + 12 of the K and of the V
+  // tile.  Lane l of slice s writes LDS chunk 64 s + l, i.e. row 8 s + l / 8 at physical
+  // chunk l % 8, which holds the row's logical chunk (l % 8) ^ swizzle(row): the swizzle is
+  // applied on the global side.  The buffer resources are based at this head's first byte and range checked
   // against the end of the tensor (rows past it read as zero).
   auto make_rsrc = [&](const void* t) __attribute__((always_inline)) -> i32x4 {
     const uint64_t a = reinterpret_cast<uint64_t>(t) + uint64_t(head) * kD;
@@ -127,10 +132,11 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
   // a buffer load may read an SGPR written by a vector instruction (the readfirstlane) only
   // 5 wait states later; the loads are inline asm, unseen by the compiler's hazard checks
   asm volatile("s_nop 4" : "+s"(rsrc_k), "+s"(rsrc_v));
-  uint32_t dk[2], dv[2];  // byte offsets of the lane's 16 bytes within a tile (slices w, w + 8)
+  constexpr int kSl = kTileB / 1024 / kWaves;  // 1 KB slices of a tile per wave
+  uint32_t dk[kSl], dv[kSl];  // byte offsets of the lane's 16 bytes within a tile
 #pragma unroll
-  for (int x = 0; x < 2; ++x) {
-    const int row = 8 * (wave + 8 * x) + (lane >> 3);
+  for (int x = 0; x < kSl; ++x) {
+    const int row = 8 * (wave + kWaves * x) + (lane >> 3);
     dk[x] = uint32_t(row) * uint32_t(row_stride) + uint32_t(((lane & 7) ^ ((row >> 1) & 7)) << 4);
     dv[x] = uint32_t(row) * uint32_t(row_stride) +
             uint32_t(((lane & 7) ^ (2 * (((row >> 1) & 1) | ((row >> 2) & 2)))) << 4);
@@ -141,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
     tile_range(t, n0, nend);
     const uint32_t toff = uint32_t(n0) * uint32_t(row_stride);
 #pragma unroll
-    for (int x = 0; x < 2; ++x) {
-      const uint32_t lk = lds_base + uint32_t(buf * kBufB + (wave + 8 * x) * 1024);
+    for (int x = 0; x < kSl; ++x) {
+      const uint32_t lk = lds_base + uint32_t(buf * kBufB + (wave + kWaves * x) * 1024);
       const uint32_t lv = lk + kTileB;
       asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(dk[x] + toff), "s"(rsrc_k), "{m0}"(lk)
                    : "memory");
@@ -154,7 +160,8 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
   dma_tile(0, 0);
 
   // Q fragments: lane = query row, bytes [64 s + 32 hh, +32) of the row for k-step s
-  const int qrow = it.q_begin + wave * 32 + l32;
+  const int wrow0 = it.q_begin + part * kRows + wave * 32;  // the wave's first row
+  const int qrow = wrow0 + l32;
   const bool q_ok = qrow < it.q_end;
   i32x8 qf[2];
   {
@@ -211,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void attn_fp8_kernel(Fp8Args p) {
       }
     }
     // mask keys past the segment end (and, for causal items, after the lane's own row)
-    const bool need_mask = valid < kBN || (causal && n0 + kBN - 1 > it.q_begin + wave * 32);
+    const bool need_mask = valid < kBN || (causal && n0 + kBN - 1 > wrow0);
     if (need_mask) {
       int lim = valid;
       if (causal) lim = __builtin_elementwise_min(lim, qrow - n0 + 1);
@@ -347,7 +354,7 @@ __global__ __launch_bounds__(64) void combine_fp8_kernel(const float* __restrict
 
 hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream) {
   if (a.d != kD) return hipErrorInvalidValue;
-  const int grid = kXcdCount * a.per_xcd;
+  const int grid = kXcdCount * a.per_xcd * kHalves;
   if (grid < 1) return hipSuccess;
   hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(kThreads), 2 * kBufB, stream, a);
   hipError_t e = hipGetLastError();
