@@ -340,7 +340,8 @@ def main() -> int:
     algo_bytes = 4 * w.L * w.H * w.d * elem + 2 * info["workspace_bytes"]
     traffic, traffic_rec = recorded_traffic(w.name)
     res = {
-        "metric": "kept-pair TFLOP/s at the H3-scale window call on 1 MI355X",
+        "metric": ("kept-pair TFLOP/s at the H3-scale window call on 1 MI355X" if w.name.startswith("h3")
+                   else f"kept-pair TFLOP/s of the {w.name} attention call on 1 MI355X"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
