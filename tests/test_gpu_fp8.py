@@ -69,9 +69,10 @@ def test_fp8_full_parity_small(gpu_lib):
     _check(got, ref, np.nanmax(np.abs(decode_e4m3(v8))) * sv, "small")
 
 
-@pytest.mark.parametrize("name", ["ragged", "h3"])
+@pytest.mark.parametrize("name", ["ragged", "h3", "h3_full"])
 def test_fp8_sampled_parity(gpu_lib, name):
-    """Sampled rows (first, last, frame and group edges, global rows, random) of every head."""
+    """Sampled rows (first, last, frame and group edges, global rows, random) of every head;
+    h3_full is the whole model's 56 heads on one GPU (the largest tensors, 709 MB each)."""
     w = WORKLOADS[name]
     _say(f"{name}: T={w.T} S={w.S} G={w.G} K={w.K} r={w.radius} H={w.H} (sampled rows)")
     q8, k8, v8, sq, sk, sv = make_fp8_inputs(w, seed=1)
