@@ -41,50 +41,61 @@ def _parse():
     ap.add_argument("--op", default="attention", choices=["attention", "prologue", "fp8"],
                     help="attention: wa_forward (default); prologue: wa_qk_norm_rope; fp8: wa_forward_fp8")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
-    ap.add_argument("--cpu-heads", type=int, default=3, help="heads of the workload the CPU oracle runs")
+    ap.add_argument("--cpu-heads", type=int, default=0,
+                    help="heads of the workload the CPU oracle runs (0: all, at most 16)")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows the CPU oracle runs for --op prologue (0: all)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="first run a plain device copy of q (known bytes) to calibrate HBM byte counters")
     return ap.parse_args()
 
 
-def _cpu_threads() -> int:
-    try:
-        from threadpoolctl import threadpool_info
+def _pool_size() -> int:
+    """Worker threads for the CPU oracle: the cores this process may use, at most 16 (the
+    host share of one GPU on a shared node)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
-        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
-        pass
-    return len(os.sched_getaffinity(0))
+
+def _by_heads(fn, q, k, v, heads: int, *args):
+    """Run `fn` (an oracle function over [L, H', d] tensors) on heads 0..heads-1, one head per
+    task, in a pool of worker threads with one BLAS thread each (numpy releases the
+    interpreter lock inside its products and exponentials).  Returns (seconds, threads)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    threads = min(_pool_size(), heads)
+    with threadpool_limits(1):
+        with ThreadPoolExecutor(threads) as ex:
+            t0 = time.perf_counter()
+            list(ex.map(lambda h: fn(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], *args), range(heads)))
+            dt = time.perf_counter() - t0
+    return dt, threads
 
 
 def cpu_baseline(w, q, k, v, heads: int) -> dict:
-    """Time the fp64 oracle (as it stands) on the first `heads` heads of the workload."""
-    import numpy as np  # noqa: F401
-
+    """Time the fp64 oracle (as it stands) on the first `heads` heads of the workload, all
+    rows, one head per task in a pool of worker threads."""
     from oracle import (Geometry, causal_attention_reference, causal_pairs_per_head, kept_pairs_per_head,
                         window_attention_reference)
 
-    qs, ks, vs = (x[:, :heads].contiguous() for x in (q, k, v))
-    t0 = time.perf_counter()
+    heads = max(1, min(heads, w.H))
     if w.causal:
-        causal_attention_reference(qs, ks, vs)
+        dt, threads = _by_heads(causal_attention_reference, q, k, v, heads)
         pairs = causal_pairs_per_head(w.L)
     else:
         geom = Geometry(*w.geometry)
-        window_attention_reference(qs, ks, vs, geom)
+        dt, threads = _by_heads(window_attention_reference, q, k, v, heads, geom)
         pairs = kept_pairs_per_head(geom)
-    dt = time.perf_counter() - t0
     flop = pairs * heads * 4 * w.d
     return {
         "value": round(flop / dt / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": _cpu_threads(),
+        "cores": threads,
+        "host_cores": len(os.sched_getaffinity(0)),
         "kind": "oracle",
-        "sample": f"fp64 numpy {'causal' if w.causal else 'per-frame'} oracle on {heads} of {w.H} heads of the {w.name} workload "
-                  f"(all {w.L} rows), {dt:.1f} s wall",
+        "sample": f"fp64 numpy {'causal' if w.causal else 'per-frame'} oracle on {heads} of {w.H} heads of the "
+                  f"{w.name} workload (all {w.L} rows), one head per worker thread, {threads} threads with one "
+                  f"BLAS thread each, {dt:.1f} s wall",
         "seconds": round(dt, 3),
     }
 
@@ -188,7 +199,9 @@ def bench_fp8(args, w) -> int:
         "plan_create_ms": round(plan_ms, 3),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_fp8_kernel (+ split merge) per wa_forward_fp8 call, HIP events on the launch stream",
+            "kernel": "attn_fp8_kernel, then its merge kernel when the global leg is split: one wa_forward_fp8 call",
+            "duration": "mean HIP-event time of the timed wa_forward_fp8 calls, events recorded on the launch "
+                        "stream around each call (both kernels)",
             "achieved": round(achieved, 2),
             "peak": MFMA_FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -203,7 +216,7 @@ def bench_fp8(args, w) -> int:
         from oracle import decode_e4m3
 
         vals = [torch.from_numpy(decode_e4m3(c) * s) for c, s in ((q8c, sq), (k8c, sk), (v8c, sv))]
-        res["cpu_baseline"] = cpu_baseline(w, *vals, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(w, *vals, args.cpu_heads or min(16, w.H))
         res["cpu_baseline"]["sample"] += " (decoded fp8 inputs)"
     print(json.dumps(res), flush=True)
     return 0
@@ -255,7 +268,8 @@ def bench_prologue(args, w) -> int:
                         "mean": round(statistics.fmean(per_call), 5)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "qk_norm_rope_kernel per wa_qk_norm_rope call, HIP events on the launch stream",
+            "kernel": "qk_norm_rope_kernel: one wa_qk_norm_rope call",
+            "duration": "mean HIP-event time of the timed calls, events recorded on the launch stream",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -276,10 +290,11 @@ def bench_prologue(args, w) -> int:
         res["cpu_baseline"] = {
             "value": round(prologue_bytes(n, w.H, w.d, elem, True) / dt / 1e9, 4),
             "unit": "GB/s",
-            "cores": _cpu_threads(),
+            "cores": 1,
+            "host_cores": len(os.sched_getaffinity(0)),
             "kind": "oracle",
-            "sample": f"fp64 numpy oracle on the first {n} of {w.L} rows (all {w.H} heads, q and k), "
-                      f"{dt:.2f} s wall",
+            "sample": f"fp64 numpy oracle on the first {n} of {w.L} rows (all {w.H} heads, q and k), one thread "
+                      f"with one BLAS thread, {dt:.2f} s wall",
             "seconds": round(dt, 3),
         }
     print(json.dumps(res), flush=True)
@@ -364,7 +379,9 @@ def main() -> int:
         "plan_create_ms": round(plan_ms, 3),
         "roofline": {
             "bound": "mfma",
-            "kernel": "attn_kernel (+ split merge) per wa_forward call, HIP events on the launch stream",
+            "kernel": "attn_kernel, then combine_kernel when the global leg is split: one wa_forward call",
+            "duration": "mean HIP-event time of the timed wa_forward calls, events recorded on the launch "
+                        "stream around each call (both kernels)",
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -376,7 +393,7 @@ def main() -> int:
         },
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_heads)
+        res["cpu_baseline"] = cpu_baseline(w, q_cpu, k_cpu, v_cpu, args.cpu_heads or min(16, w.H))
     print(json.dumps(res), flush=True)
     return 0
 

@@ -200,6 +200,10 @@ def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
     q, k, v: contiguous CUDA (HIP) tensors [L, H, d] of one dtype, bfloat16 or float32.
     ``stream``: a torch stream (default: the current stream).
     """
+    return _forward("wa_forward", plan, q, k, v, out, stream)
+
+
+def _forward(entry: str, plan: Plan, q, k, v, out, stream):
     import torch
 
     info = plan.info
@@ -224,8 +228,8 @@ def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
         stream = torch.cuda.current_stream(q.device)
     code = WA_F32 if dtype == torch.float32 else WA_BF16
     with torch.cuda.device(q.device):
-        _check(load_library().wa_forward(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
-                                         code, ctypes.c_void_p(stream.cuda_stream)))
+        _check(getattr(load_library(), entry)(plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                              code, ctypes.c_void_p(stream.cuda_stream)))
     return out
 
 

@@ -6,14 +6,18 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <list>
 #include <map>
 #include <memory>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "wa.h"
 #include "launch.h"
@@ -34,15 +38,25 @@ struct DeviceResources {
   void* staging = nullptr;   // bf16 copies of fp32 q, k, v (allocated on first fp32 call)
   int64_t staging_bytes = 0;
   int n_cus = 0;             // compute units of the device: one persistent block each
+  // Ordering of calls that share this plan's tables, queue counters and workspace: the
+  // event is recorded on the stream of the last call, and a call on another stream first
+  // makes its stream wait for it.
+  hipEvent_t done = nullptr;
+  hipStream_t last_stream = nullptr;
+  bool launched = false;
 };
 
 }  // namespace
 
 struct wa_plan {
   wa::HostPlan host;
+  // Image of the plan's device tables as int32: the work items, the launch order, then
+  // kXcdCount + 1 zeroed work-queue counters (uploaded as one block).
+  std::vector<int32_t> table;
   std::atomic<int> refs{1};
   std::atomic<bool> cached{true};
-  std::mutex dev_mu;
+  std::mutex dev_mu;     // creation of device resources, staging growth
+  std::mutex launch_mu;  // stream ordering + launches of one call (see DeviceResources::done)
   std::map<int, DeviceResources> dev;
 
   ~wa_plan() {
@@ -53,6 +67,7 @@ struct wa_plan {
       if (kv.second.items) (void)hipFree(kv.second.items);
       if (kv.second.part) (void)hipFree(kv.second.part);
       if (kv.second.staging) (void)hipFree(kv.second.staging);
+      if (kv.second.done) (void)hipEventDestroy(kv.second.done);
     }
     if (prev >= 0) (void)hipSetDevice(prev);
   }
@@ -62,7 +77,10 @@ namespace {
 
 constexpr size_t kCacheCapacity = 4;
 std::mutex g_cache_mu;
-std::list<wa_plan*> g_cache;  // front = most recently created or fetched
+// Front = most recently created or fetched.  Cached plans live until the process ends: the
+// list is never destroyed (no plan is freed during static destruction, when the HIP
+// runtime may already be gone), so the plans it holds stay reachable to the end.
+std::list<wa_plan*>& g_cache = *new std::list<wa_plan*>;
 
 void unref(wa_plan* p) {
   if (p->refs.fetch_sub(1) == 1) delete p;
@@ -83,23 +101,26 @@ int device_resources(wa_plan* p, DeviceResources** out) {
   e = hipDeviceGetAttribute(&r.n_cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess || r.n_cus < 1) return fail(WA_ERR_HIP, "hipDeviceGetAttribute(multiprocessor count) failed");
   // items, then the launch order (int32), then the work-queue counters, in one allocation
-  const size_t item_bytes = p->host.items.size() * sizeof(wa::Item);
-  const size_t work_bytes = p->host.work.size() * sizeof(int32_t);
-  const size_t counter_bytes = (wa::kXcdCount + 1) * sizeof(int32_t);
-  e = hipMalloc(&r.items, item_bytes + work_bytes + counter_bytes);
+  // filled by one blocking copy (the counters must read zero before the first launch, on
+  // whatever stream it comes)
+  const size_t table_bytes = p->table.size() * sizeof(int32_t);
+  e = hipMalloc(&r.items, table_bytes);
   if (e != hipSuccess) return fail(WA_ERR_ALLOC, std::string("hipMalloc(items): ") + hipGetErrorString(e));
-  e = hipMemcpy(r.items, p->host.items.data(), item_bytes, hipMemcpyHostToDevice);
-  if (e == hipSuccess)
-    e = hipMemcpy(reinterpret_cast<char*>(r.items) + item_bytes, p->host.work.data(), work_bytes, hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(reinterpret_cast<char*>(r.items) + item_bytes + work_bytes, 0, counter_bytes);
+  e = hipMemcpy(r.items, p->table.data(), table_bytes, hipMemcpyHostToDevice);
   if (e != hipSuccess) {
     (void)hipFree(r.items);
     return fail(WA_ERR_HIP, std::string("hipMemcpy(items): ") + hipGetErrorString(e));
+  }
+  e = hipEventCreateWithFlags(&r.done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)hipFree(r.items);
+    return fail(WA_ERR_HIP, std::string("hipEventCreate: ") + hipGetErrorString(e));
   }
   if (p->host.partial_bytes > 0) {
     e = hipMalloc(&r.part, (size_t)p->host.partial_bytes);
     if (e != hipSuccess) {
       (void)hipFree(r.items);
+      (void)hipEventDestroy(r.done);
       return fail(WA_ERR_ALLOC, std::string("hipMalloc(workspace): ") + hipGetErrorString(e));
     }
   }
@@ -112,6 +133,38 @@ bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15u) ==
 bool overlaps(const void* a, const void* b, size_t n) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + n && y < x + n;
+}
+
+// Enqueue one call's work that uses the plan's device tables, queue counters and workspace:
+// under the plan's launch lock, when the plan's previous call went to another stream, make
+// `stream` wait for it first; then run `enqueue` and record the plan's event on `stream`.
+// Calls that share a plan (equal geometries share one) so never overlap on the device.
+template <class F>
+int ordered_launch(wa_plan* p, DeviceResources* r, hipStream_t stream, const char* who, F&& enqueue) {
+  std::lock_guard<std::mutex> lk(p->launch_mu);
+  if (r->launched && r->last_stream != stream) {
+    const hipError_t e = hipStreamWaitEvent(stream, r->done, 0);
+    if (e != hipSuccess) return fail(WA_ERR_HIP, std::string(who) + ": hipStreamWaitEvent: " + hipGetErrorString(e));
+  }
+  const int st = enqueue();
+  if (st != WA_OK) return st;
+  const hipError_t e = hipEventRecord(r->done, stream);
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string(who) + ": hipEventRecord: " + hipGetErrorString(e));
+  r->launched = true;
+  r->last_stream = stream;
+  return WA_OK;
+}
+
+// One-line summary of a newly built plan on stderr when the environment sets WA_LOG=1.
+void log_plan(const wa::HostPlan& h, double build_us) {
+  const char* env = std::getenv("WA_LOG");
+  if (!env || std::strcmp(env, "1") != 0) return;
+  std::fprintf(stderr,
+               "wa: plan %s T=%d S=%d G=%d K=%d radius=%d H=%d d=%d: L=%d chunks=%d groups=%zu items=%zu "
+               "(window %d) splits=%d queue=%dx%d kept_pairs/head=%lld workspace=%lld B, built in %.0f us\n",
+               h.geo.causal ? "causal" : "window", h.geo.T, h.geo.S, h.geo.G, h.geo.K, h.geo.radius, h.geo.H,
+               h.geo.d, h.L, h.n_chunks, h.groups.size(), h.items.size(), h.n_window_items, h.n_splits, wa::kXcdCount,
+               h.work_per_xcd, (long long)h.kept_pairs_per_head, (long long)h.partial_bytes, build_us);
 }
 
 }  // namespace
@@ -137,8 +190,10 @@ static int create_cached(const wa::Geometry& geo, wa_plan** out, const char* who
   }
   wa::HostPlan hp;
   std::string err;
+  const auto t0 = std::chrono::steady_clock::now();
   const int st = geo.causal ? wa::build_causal_plan(geo.S, geo.H, geo.d, &hp, &err) : wa::build_plan(geo, &hp, &err);
   if (st != 0) return fail(st, std::string(who) + ": " + err);
+  log_plan(hp, std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count());
   wa_plan* p = nullptr;
   try {
     p = new wa_plan();
@@ -146,6 +201,13 @@ static int create_cached(const wa::Geometry& geo, wa_plan** out, const char* who
     return fail(WA_ERR_ALLOC, std::string(who) + ": out of host memory");
   }
   p->host = std::move(hp);
+  {
+    const wa::HostPlan& h = p->host;
+    const size_t item_words = h.items.size() * (sizeof(wa::Item) / sizeof(int32_t));
+    p->table.assign(item_words + h.work.size() + (wa::kXcdCount + 1), 0);
+    std::memcpy(p->table.data(), h.items.data(), item_words * sizeof(int32_t));
+    std::memcpy(p->table.data() + item_words, h.work.data(), h.work.size() * sizeof(int32_t));
+  }
   p->refs.store(2);  // the caller's handle + the cache's
   wa_plan* evicted = nullptr;
   {
@@ -254,30 +316,92 @@ int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n) {
   return WA_OK;
 }
 
+// Argument checks of wa_forward.
+static int check_forward(const char* who, const wa_plan* plan, const void* q, const void* k, const void* v,
+                         const void* out, int dtype) {
+  if (!plan) return fail(WA_ERR_INVALID, std::string(who) + ": plan is NULL");
+  if (!q || !k || !v || !out) return fail(WA_ERR_INVALID, std::string(who) + ": NULL tensor pointer");
+  if (dtype != WA_BF16 && dtype != WA_F32)
+    return fail(WA_ERR_INVALID, std::string(who) + ": dtype must be WA_BF16 or WA_F32");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(WA_ERR_INVALID, std::string(who) + ": tensors must be 16-byte aligned");
+  const wa::HostPlan& h = plan->host;
+  const size_t bytes = size_t(int64_t(h.L) * h.geo.H * h.geo.d) * (dtype == WA_F32 ? 4 : 2);
+  if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
+    return fail(WA_ERR_INVALID, std::string(who) + ": out overlaps an input");
+  return WA_OK;
+}
+
+// Launch arguments of `h` with its device tables at `table` (the int32 image of
+// wa_plan::table) and the global leg's partials at `part` (may be NULL without splits).
+static wa::ForwardArgs forward_args(const wa::HostPlan& h, int32_t* table, float* part, int n_cus, void* out,
+                                    int dtype) {
+  wa::ForwardArgs a;
+  a.q = a.k = a.v = nullptr;
+  a.out = out;
+  a.out_f32 = dtype == WA_F32;
+  a.d = h.geo.d;
+  a.H = h.geo.H;
+  a.L = h.L;
+  a.G = h.geo.G;
+  a.frame_rows = h.n_frame_rows;
+  a.block_m = h.block_m;
+  a.items = reinterpret_cast<const wa::Item*>(table);
+  a.n_items = (int)h.items.size();
+  a.work = table + h.items.size() * (sizeof(wa::Item) / sizeof(int32_t));
+  a.work_per_xcd = h.work_per_xcd;
+  a.counters = const_cast<int32_t*>(a.work) + h.work.size();
+  // Persistent blocks pay a few memory round trips per unit for the queues; they pay off only
+  // when each CU runs several units.  Otherwise one block per unit.
+  const int64_t units = int64_t(h.items.size()) * h.geo.H;
+  a.persistent = units > 2 * int64_t(n_cus) ? 1 : 0;
+  a.grid = a.persistent ? n_cus : wa::kXcdCount * h.work_per_xcd;
+  a.n_splits = h.n_splits;
+  a.part_o = part;
+  a.part_ml = part ? part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;
+  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(h.geo.d)));
+  return a;
+}
+
+// Enqueue one call: for fp32 inputs their bf16 copies into `staging` (3 * elems * 2 bytes),
+// then the attention and the merge.
+static int enqueue_forward(const char* who, wa::ForwardArgs a, const void* q, const void* k, const void* v, int dtype,
+                           char* staging, int64_t elems, hipStream_t stream) {
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  if (dtype == WA_F32) {
+    const void* src[3] = {q, k, v};
+    for (int i = 0; i < 3; ++i) {
+      hipError_t e = wa::launch_f32_to_bf16(static_cast<const float*>(src[i]), staging + i * elems * 2, elems, stream);
+      if (e != hipSuccess) return fail(WA_ERR_HIP, std::string(who) + ": f32_to_bf16 launch: " + hipGetErrorString(e));
+    }
+    a.q = staging;
+    a.k = staging + elems * 2;
+    a.v = staging + 2 * elems * 2;
+  }
+  hipError_t e = wa::launch_forward(a, stream);
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string(who) + ": launch: " + hipGetErrorString(e));
+  return WA_OK;
+}
+
 int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v, void* out, int dtype,
                void* stream_v) {
-  if (!cplan) return fail(WA_ERR_INVALID, "wa_forward: plan is NULL");
-  if (!q || !k || !v || !out) return fail(WA_ERR_INVALID, "wa_forward: NULL tensor pointer");
-  if (dtype != WA_BF16 && dtype != WA_F32) return fail(WA_ERR_INVALID, "wa_forward: dtype must be WA_BF16 or WA_F32");
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
-    return fail(WA_ERR_INVALID, "wa_forward: tensors must be 16-byte aligned");
+  int st = check_forward("wa_forward", cplan, q, k, v, out, dtype);
+  if (st != WA_OK) return st;
   wa_plan* plan = const_cast<wa_plan*>(cplan);
   const wa::HostPlan& h = plan->host;
   const int64_t elems = int64_t(h.L) * h.geo.H * h.geo.d;
-  const size_t esize = dtype == WA_F32 ? 4 : 2;
-  const size_t bytes = size_t(elems) * esize;
-  if (overlaps(out, q, bytes) || overlaps(out, k, bytes) || overlaps(out, v, bytes))
-    return fail(WA_ERR_INVALID, "wa_forward: out overlaps an input");
   hipStream_t stream = static_cast<hipStream_t>(stream_v);
 
   DeviceResources* r = nullptr;
-  int st = device_resources(plan, &r);
+  st = device_resources(plan, &r);
   if (st != WA_OK) return st;
+  const wa::ForwardArgs a = forward_args(h, reinterpret_cast<int32_t*>(r->items), r->part, r->n_cus, out, dtype);
 
-  const void *qb = q, *kb = k, *vb = v;
-  if (dtype == WA_F32) {
-    const int64_t need = 3 * elems * 2;
-    {
+  return ordered_launch(plan, r, stream, "wa_forward", [&]() -> int {
+    if (dtype == WA_F32) {
+      const int64_t need = 3 * elems * 2;
       std::lock_guard<std::mutex> lk(plan->dev_mu);
       if (r->staging_bytes < need) {
         if (r->staging) (void)hipFree(r->staging);
@@ -288,46 +412,8 @@ int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v
         r->staging_bytes = need;
       }
     }
-    char* s = static_cast<char*>(r->staging);
-    const void* src[3] = {q, k, v};
-    for (int i = 0; i < 3; ++i) {
-      hipError_t e = wa::launch_f32_to_bf16(static_cast<const float*>(src[i]), s + i * elems * 2, elems, stream);
-      if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("f32_to_bf16 launch: ") + hipGetErrorString(e));
-    }
-    qb = s;
-    kb = s + elems * 2;
-    vb = s + 2 * elems * 2;
-  }
-
-  wa::ForwardArgs a;
-  a.q = qb;
-  a.k = kb;
-  a.v = vb;
-  a.out = out;
-  a.out_f32 = dtype == WA_F32;
-  a.d = h.geo.d;
-  a.H = h.geo.H;
-  a.L = h.L;
-  a.G = h.geo.G;
-  a.frame_rows = h.n_frame_rows;
-  a.block_m = h.block_m;
-  a.items = r->items;
-  a.n_items = (int)h.items.size();
-  a.work = reinterpret_cast<const int32_t*>(r->items + h.items.size());
-  a.work_per_xcd = h.work_per_xcd;
-  a.counters = const_cast<int32_t*>(a.work) + h.work.size();
-  // Persistent blocks pay a few memory round trips per unit for the queues; they pay off only
-  // when each CU runs several units.  Otherwise one block per unit.
-  const int64_t units = int64_t(h.items.size()) * h.geo.H;
-  a.persistent = units > 2 * int64_t(r->n_cus) ? 1 : 0;
-  a.grid = a.persistent ? r->n_cus : wa::kXcdCount * h.work_per_xcd;
-  a.n_splits = h.n_splits;
-  a.part_o = r->part;
-  a.part_ml = r->part ? r->part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;
-  a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(h.geo.d)));
-  hipError_t e = wa::launch_forward(a, stream);
-  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward launch: ") + hipGetErrorString(e));
-  return WA_OK;
+    return enqueue_forward("wa_forward", a, q, k, v, dtype, static_cast<char*>(r->staging), elems, stream);
+  });
 }
 
 int wa_forward_fp8(const wa_plan* cplan, const void* q, const void* k, const void* v, float scale_q, float scale_k,
@@ -371,9 +457,12 @@ int wa_forward_fp8(const wa_plan* cplan, const void* q, const void* k, const voi
   a.part_ml = r->part ? r->part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;
   a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(h.geo.d)) * double(scale_q) * double(scale_k));
   a.scale_v = scale_v;
-  hipError_t e = wa::launch_forward_fp8(a, static_cast<hipStream_t>(stream_v));
-  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward_fp8 launch: ") + hipGetErrorString(e));
-  return WA_OK;
+  const hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  return ordered_launch(plan, r, stream, "wa_forward_fp8", [&]() -> int {
+    hipError_t e = wa::launch_forward_fp8(a, stream);
+    if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward_fp8 launch: ") + hipGetErrorString(e));
+    return WA_OK;
+  });
 }
 
 int wa_qk_norm_rope(const void* q, const void* k, void* q_out, void* k_out, const float* cos, const float* sin,

@@ -265,7 +265,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(Fp8Args p) {
       const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt), __builtin_bit_cast(uint32_t, mt),
                                                       false, false);
       mt = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-      const float m_new = __builtin_fmaxf(m_run, mt * c);
+      // Per row: the max rises only where the tile's weights could exceed 2^8 against it
+      // (and on the first tile), so a row's weights never depend on the other rows' scores.
+      const float m_new = mt * c > m_run + 8.f ? mt * c : m_run;
       const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
       l_run *= alpha;
 #pragma unroll

@@ -37,8 +37,8 @@
 //   XOR-swizzled per row (applied on the global side of the DMA) so the K reads and the
 //   transpose reads are free of bank conflicts.
 //   The running max is raised lazily: exponentials are taken against the running max,
-//   and a wave-uniform slow path raises it (rescaling the accumulators) only when some
-//   row's max grew by more than 2^8 (values up to 2^8 are exact in the softmax ratio);
+//   and a wave-uniform slow path raises the max of each row whose max grew by more than
+//   2^8 (rescaling its accumulators; values up to 2^8 are exact in the softmax ratio);
 //   the same path masks keys past a segment end.  Whether a tile needs it for reasons other
 //   than its data (first tile, masked keys) is known before the tile: one scalar compare.
 //   The launch is persistent: one block per CU takes work units from its XCD's queue in the
@@ -439,8 +439,12 @@ void attn_kernel(AttnParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
     mt = pair_max(mt);
-    if (__builtin_amdgcn_ballot_w64(mt > m_run[qb] + lazy_raw) != 0) {
-      const float m_new = __builtin_fmaxf(m_run[qb], mt);
+    // Only rows whose own max grew by more than 2^8 raise it (the branch is wave-uniform,
+    // the choice per row): the other rows keep their max and rescale by exactly 1, so a
+    // row's arithmetic never depends on the scores of the other rows in the wave.
+    const bool grow = mt > m_run[qb] + lazy_raw;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m_run[qb];
       const float alpha = fast_exp2((m_run[qb] - m_new) * c2);
       m_run[qb] = m_new;
       mc[qb] = m_new * c2;

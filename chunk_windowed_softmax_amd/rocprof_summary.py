@@ -60,12 +60,15 @@ def _short(name: str) -> str:
     return name[:60]
 
 
-def trace_durations(trace_dir: str) -> Dict[str, List[float]]:
+def trace_durations(trace_dir: str, skip: int = 0) -> Dict[str, List[float]]:
+    """Dispatch durations (ns) per kernel in launch order, without the first `skip`
+    dispatches of each kernel (the untimed warm-up calls of a bench run)."""
     rows = _rows(os.path.join(trace_dir, "**", "*kernel_trace.csv"))
+    rows.sort(key=lambda r: float(r["Start_Timestamp"]))
     d: Dict[str, List[float]] = {}
     for r in rows:
         d.setdefault(_short(r["Kernel_Name"]), []).append(float(r["End_Timestamp"]) - float(r["Start_Timestamp"]))
-    return d
+    return {k: v[skip:] if len(v) > skip else v for k, v in d.items()}
 
 
 def counter_means(pmc_dir: str, counter: str) -> Dict[str, float]:
@@ -112,10 +115,14 @@ def main() -> int:
     ap.add_argument("--xcds", type=int, default=8)
     ap.add_argument("--simds", type=int, default=1024)
     ap.add_argument("--cus", type=int, default=256)
+    ap.add_argument("--skip", type=int, default=0,
+                    help="dispatches of each kernel to drop from the trace statistics (the warm-up calls)")
+    ap.add_argument("--per-call", default="",
+                    help="comma-separated kernels that one call launches, summed per call (e.g. attn_kernel,combine_kernel)")
     a = ap.parse_args()
     kern = a.kernel  # the profiled kernel
 
-    dur = trace_durations(a.trace)
+    dur = trace_durations(a.trace, a.skip)
     fetch = counter_means(a.fetch, "FETCH_SIZE")
     write = counter_means(a.write, "WRITE_SIZE")
     copy_kib = a.copy_bytes / 1024.0
@@ -142,7 +149,15 @@ def main() -> int:
         "algorithmic_bytes": a.algorithmic_bytes,
         "hbm_gbs_at_avg_duration": (attn_fetch + attn_write) / (attn_ns * 1e-9) / 1e9,
         "algorithmic_gbs_at_avg_duration": a.algorithmic_bytes / (attn_ns * 1e-9) / 1e9,
+        "skipped_dispatches_per_kernel": a.skip,
     }
+    call_kernels = [x for x in a.per_call.split(",") if x]
+    if call_kernels:
+        call_ns = sum(statistics.fmean(dur[x]) for x in call_kernels if x in dur)
+        res["per_call_kernels"] = call_kernels
+        res["per_call_avg_ms"] = call_ns / 1e6
+        if a.flop_per_call:
+            res["tflops_at_per_call_avg"] = a.flop_per_call / (call_ns * 1e-9) / 1e12
     sq_lines = []
     if a.sq:
         sq = sq_means(a.sq)[kern]
@@ -177,6 +192,9 @@ def main() -> int:
         f"- FETCH_SIZE:   `{a.command_fetch}`",
         f"- WRITE_SIZE:   `{a.command_write}`",
         "",
+        (f"Statistics over the timed calls: the first {a.skip} dispatches of each kernel (the warm-up "
+         "calls) are dropped." if a.skip else "Statistics over all dispatches."),
+        "",
         "| kernel | calls | avg ms | median ms | min ms | max ms |",
         "|---|---|---|---|---|---|",
     ]
@@ -186,6 +204,9 @@ def main() -> int:
     if a.flop_per_call:
         lines += ["", f"Kept-pair FLOP per call: {a.flop_per_call:.6g}; at the average `{kern}` duration: "
                   f"{res['tflops_at_avg_duration']:.1f} TFLOP/s."]
+    if call_kernels:
+        lines += ["", f"One call ({' + '.join(call_kernels)}): {res['per_call_avg_ms']:.4f} ms on average"
+                  + (f", {res['tflops_at_per_call_avg']:.1f} TFLOP/s." if a.flop_per_call else ".")]
     lines += [
         "",
         f"Algorithmic bytes per call: {a.algorithmic_bytes:.6g}; at the average `{kern}` duration: "

@@ -97,7 +97,9 @@ enum {
  * Arguments: T, S, K, H >= 1; G >= 0; radius >= 0; d in {64, 128}; L*H*d < 2^31.
  * On success *out receives a handle that the caller owns one reference of; release it
  * with wa_plan_release.  Building a plan touches no device: device tables and the
- * workspace are created on the first wa_forward on each device.
+ * workspace are created on the first wa_forward on each device.  With the environment
+ * variable WA_LOG=1, building a plan (a cache miss) prints a one-line summary of it
+ * (groups, items, splits, launch queues, kept pairs, workspace bytes, build time) to stderr.
  * Errors: WA_ERR_INVALID (bad geometry or out == NULL), WA_ERR_UNSUPPORTED (d, index
  * range), WA_ERR_ALLOC.
  */
@@ -134,8 +136,12 @@ int wa_plan_release(wa_plan* plan);
  * default stream); all work is enqueued on it and the call returns without
  * synchronising.  The first call on a device allocates the plan's device tables and
  * workspace (and, for WA_F32, a bf16 staging copy of q, k, v); later calls allocate
- * nothing.  Concurrent calls with one plan on different streams race on the plan's
- * workspace: serialise them.  Every element of q, k and v must be finite: key tiles are
+ * nothing.  Equal geometries share one cached plan, and with it one set of device tables,
+ * work-queue counters and workspace: the library orders calls that use one plan, so a
+ * call on a stream other than that of the plan's previous call (from any handle, through
+ * wa_forward or wa_forward_fp8) first makes its stream wait for that call to finish.
+ * Calls that use one plan on different streams therefore do not overlap on the device.
+ * Every element of q, k and v must be finite: key tiles are
  * read whole, so rows next to a row's kept keys are read and masked to zero weight, and a
  * NaN or infinity there would still reach the output (finite values never do).
  * Errors: WA_ERR_INVALID (NULL / misaligned / overlapping pointers, bad dtype),
@@ -148,7 +154,10 @@ int wa_forward(const wa_plan* plan, const void* q, const void* k, const void* v,
 int wa_plan_info(const wa_plan* plan, wa_plan_info_t* info);
 
 /*
- * wa_plan_groups -- copy the window groups to host memory: n_groups rows of six int32
+ * wa_plan_groups -- copy the window groups of the decomposed form (§三: query rows whose
+ * kept-KV sets are identical form one group, one dense attention each; for frame rows that
+ * is a maximal run of consecutive chunks sharing one window of §一) to host memory:
+ * n_groups rows of six int32
  * {q_begin, q_end, kv_begin, kv_end, chunk_lo, chunk_hi}; rows [q_begin, q_end) attend
  * to keys [kv_begin, kv_end) (the span of chunks chunk_lo..chunk_hi) plus the global
  * rows.  `n` is the capacity of dst in int32 elements; WA_ERR_INVALID if it is too small.
@@ -158,8 +167,9 @@ int wa_plan_groups(const wa_plan* plan, int32_t* dst, size_t n);
 /*
  * wa_plan_kv_indices -- copy group g's explicit ascending kept-KV index list (chunk
  * span, then the global rows) to host memory: (kv_end - kv_begin + G) int32.  These are
- * the gather indices of the decomposed form; the kernels never materialise them (they
- * read the span and the global rows in place).  WA_ERR_INVALID for a bad g or small n.
+ * the gather indices of the decomposed form (§三: each group's kept keys, its window's
+ * chunk span of §一 plus the global rows, which §五 notes the reference gathers per group);
+ * the kernels never materialise them (they read the span and the global rows in place).  WA_ERR_INVALID for a bad g or small n.
  */
 int wa_plan_kv_indices(const wa_plan* plan, int g, int32_t* dst, size_t n);
 
@@ -194,8 +204,8 @@ int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n);
  * for the second product (the one approximation beyond the inputs), the row sums over the
  * fp32 weights, output rounded to bf16.
  * stream: a hipStream_t (NULL = default).  Enqueues the kernels and returns without
- * synchronising; shares the plan's workspace with wa_forward (calls on different streams
- * that use one plan must be ordered by the caller).
+ * synchronising; shares the plan's workspace with wa_forward and is ordered with the
+ * plan's other calls in the same way (see wa_forward).
  * Errors: WA_ERR_INVALID (NULL plan or tensor, misalignment, overlap, bad scale),
  * WA_ERR_UNSUPPORTED (d != 128), WA_ERR_ALLOC, WA_ERR_HIP.
  */

@@ -1,0 +1,198 @@
+// Host-side exercise of the C ABI (include/wa.h) for the address, undefined-behaviour and
+// thread sanitizers: plan builds over a geometry sweep with every introspection call,
+// the four-plan cache with evictions while handles are outstanding, every argument error
+// path, and (with threads) concurrent create / fetch / release of shared plans.
+//
+// Usage: host_driver [threads]   -- prints "OK <checks>" and exits 0, or names the failed
+// check and exits 1.
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+#include "wa.h"
+
+static long g_checks = 0;
+#define CHECK(cond)                                                                  \
+  do {                                                                               \
+    ++g_checks;                                                                      \
+    if (!(cond)) {                                                                   \
+      std::fprintf(stderr, "FAILED %s:%d: %s (%s)\n", __FILE__, __LINE__, #cond,     \
+                   wa_last_error());                                                 \
+      std::exit(1);                                                                  \
+    }                                                                                \
+  } while (0)
+
+// Every introspection call on one plan, with buffers of exactly the needed size (so an
+// overrun is caught by the address sanitizer) and one element short (rejected).
+static void introspect(wa_plan* p) {
+  wa_plan_info_t info;
+  CHECK(wa_plan_info(p, &info) == WA_OK);
+  CHECK(info.L == info.T * info.S + info.G);
+  std::vector<int32_t> groups(size_t(info.n_groups) * 6);
+  if (!groups.empty()) {
+    CHECK(wa_plan_groups(p, groups.data(), groups.size()) == WA_OK);
+    CHECK(wa_plan_groups(p, groups.data(), groups.size() - 1) == WA_ERR_INVALID);
+  }
+  int64_t rows = 0;
+  for (int g = 0; g < info.n_groups; ++g) {
+    const int32_t* gr = &groups[size_t(g) * 6];
+    rows += gr[1] - gr[0];
+    const size_t n = size_t(gr[3] - gr[2]) + size_t(info.G);
+    std::vector<int32_t> kv(n);
+    CHECK(wa_plan_kv_indices(p, g, kv.data(), n) == WA_OK);
+    CHECK(kv.front() == gr[2] && (info.G == 0 || kv.back() == info.L - 1));
+    if (n > 1) CHECK(wa_plan_kv_indices(p, g, kv.data(), n - 1) == WA_ERR_INVALID);
+  }
+  if (!info.causal) CHECK(rows == int64_t(info.T) * info.S);
+  CHECK(wa_plan_kv_indices(p, info.n_groups, groups.data(), groups.size()) == WA_ERR_INVALID);
+  CHECK(wa_plan_kv_indices(p, -1, groups.data(), groups.size()) == WA_ERR_INVALID);
+  std::vector<int32_t> items(size_t(info.n_items) * WA_ITEM_COLS);
+  CHECK(wa_plan_items(p, items.data(), items.size()) == WA_OK);
+  CHECK(wa_plan_items(p, items.data(), items.size() - 1) == WA_ERR_INVALID);
+  const size_t nl = size_t(info.launch_xcds) * info.launch_per_xcd;
+  std::vector<int32_t> order(nl);
+  CHECK(wa_plan_launch_order(p, order.data(), nl) == WA_OK);
+  CHECK(wa_plan_launch_order(p, order.data(), nl - 1) == WA_ERR_INVALID);
+  int64_t units = 0;
+  for (int32_t u : order) units += u >= 0;
+  CHECK(units == int64_t(info.n_items) * info.H);
+}
+
+static void sweep() {
+  for (int T = 1; T <= 13; ++T)
+    for (int S = 1; S <= 3; ++S)
+      for (int K = 1; K <= 5; ++K)
+        for (int r = 0; r <= 7; r += 2)
+          for (int G = 0; G <= 3; G += 3) {
+            wa_plan* p = nullptr;
+            CHECK(wa_plan_create(T, S, G, K, r, 1 + (T % 2), T % 3 ? 64 : 128, &p) == WA_OK && p);
+            introspect(p);
+            CHECK(wa_plan_release(p) == WA_OK);
+          }
+  const int named[][7] = {{6, 16, 8, 2, 1, 1, 64},       {24, 256, 256, 3, 1, 8, 128}, {102, 960, 1024, 3, 1, 7, 128},
+                          {102, 960, 1024, 3, 1, 56, 128}, {50, 432, 77, 4, 2, 16, 128}, {8, 1024, 0, 1, 8, 16, 64}};
+  for (const auto& g : named) {
+    wa_plan* p = nullptr;
+    CHECK(wa_plan_create(g[0], g[1], g[2], g[3], g[4], g[5], g[6], &p) == WA_OK);
+    introspect(p);
+    CHECK(wa_plan_release(p) == WA_OK);
+  }
+  for (int n : {1, 37, 256, 1000, 16384}) {
+    wa_plan* p = nullptr;
+    CHECK(wa_causal_plan_create(n, 3, 64, &p) == WA_OK);
+    introspect(p);
+    CHECK(wa_plan_release(p) == WA_OK);
+  }
+}
+
+// Six distinct geometries held at once: the cache keeps four, the evicted plans stay valid
+// until their handles are released; fetching a cached geometry returns the same plan.
+static void cache() {
+  std::vector<wa_plan*> held;
+  for (int i = 0; i < 6; ++i) {
+    wa_plan* p = nullptr;
+    CHECK(wa_plan_create(10 + i, 4, 2, 2, 1, 2, 64, &p) == WA_OK);
+    held.push_back(p);
+  }
+  for (wa_plan* p : held) introspect(p);
+  wa_plan* again = nullptr;
+  CHECK(wa_plan_create(15, 4, 2, 2, 1, 2, 64, &again) == WA_OK && again == held[5]);
+  CHECK(wa_plan_release(again) == WA_OK);
+  wa_plan* rebuilt = nullptr;  // geometry 0 was evicted: a new plan
+  CHECK(wa_plan_create(10, 4, 2, 2, 1, 2, 64, &rebuilt) == WA_OK && rebuilt);
+  introspect(rebuilt);
+  introspect(held[0]);
+  CHECK(wa_plan_release(rebuilt) == WA_OK);
+  for (wa_plan* p : held) CHECK(wa_plan_release(p) == WA_OK);
+}
+
+static void errors() {
+  wa_plan* p = nullptr;
+  CHECK(wa_plan_create(0, 4, 0, 1, 0, 1, 64, &p) == WA_ERR_INVALID && p == nullptr);
+  CHECK(wa_plan_create(4, 4, -1, 1, 0, 1, 64, &p) == WA_ERR_INVALID);
+  CHECK(wa_plan_create(4, 4, 0, 0, 0, 1, 64, &p) == WA_ERR_INVALID);
+  CHECK(wa_plan_create(4, 4, 0, 1, -1, 1, 64, &p) == WA_ERR_INVALID);
+  CHECK(wa_plan_create(4, 4, 0, 1, 0, 0, 64, &p) == WA_ERR_INVALID);
+  CHECK(wa_plan_create(4, 4, 0, 1, 0, 1, 96, &p) == WA_ERR_UNSUPPORTED);
+  CHECK(wa_plan_create(1 << 15, 1 << 10, 0, 1, 0, 1, 128, &p) == WA_ERR_UNSUPPORTED);
+  CHECK(wa_plan_create(4, 4, 0, 1, 0, 1, 64, nullptr) == WA_ERR_INVALID);
+  CHECK(std::strlen(wa_last_error()) > 0);
+  CHECK(wa_causal_plan_create(0, 1, 64, &p) == WA_ERR_INVALID);
+  CHECK(wa_causal_plan_create(10, 1, 32, &p) == WA_ERR_UNSUPPORTED);
+  CHECK(wa_plan_release(nullptr) == WA_ERR_INVALID);
+  wa_plan_info_t info;
+  int32_t buf[8];
+  CHECK(wa_plan_info(nullptr, &info) == WA_ERR_INVALID);
+  CHECK(wa_plan_groups(nullptr, buf, 8) == WA_ERR_INVALID);
+  CHECK(wa_plan_kv_indices(nullptr, 0, buf, 8) == WA_ERR_INVALID);
+  CHECK(wa_plan_items(nullptr, buf, 8) == WA_ERR_INVALID);
+  CHECK(wa_plan_launch_order(nullptr, buf, 8) == WA_ERR_INVALID);
+
+  CHECK(wa_plan_create(4, 8, 2, 2, 1, 2, 64, &p) == WA_OK);
+  CHECK(wa_plan_info(p, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_plan_groups(p, nullptr, 8) == WA_ERR_INVALID);
+  // wa_forward / wa_forward_fp8 argument checks happen before any device is touched; the
+  // pointers below are never dereferenced.
+  alignas(16) static char mem[4][1 << 16];
+  void *q = mem[0], *k = mem[1], *v = mem[2], *o = mem[3];
+  CHECK(wa_forward(nullptr, q, k, v, o, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward(p, nullptr, k, v, o, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward(p, q, k, v, nullptr, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward(p, q, k, v, o, 7, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward(p, mem[0] + 2, k, v, o, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward(p, q, k, v, mem[0] + 16, WA_BF16, nullptr) == WA_ERR_INVALID);  // overlaps q
+  CHECK(wa_forward_fp8(nullptr, q, k, v, 1.f, 1.f, 1.f, o, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward_fp8(p, q, k, v, 0.f, 1.f, 1.f, o, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward_fp8(p, q, k, v, 1.f, 1.f, 1.f, o, nullptr) == WA_ERR_UNSUPPORTED);  // d = 64
+  // Valid arguments reach the HIP runtime: with no device (or with the stub launchers of
+  // this host-only build) the call fails with WA_ERR_HIP and a message, without a crash.
+  CHECK(wa_forward(p, q, k, v, o, WA_BF16, nullptr) == WA_ERR_HIP && std::strlen(wa_last_error()) > 0);
+  CHECK(wa_plan_release(p) == WA_OK);
+  const float* f = reinterpret_cast<const float*>(mem[2]);
+  CHECK(wa_qk_norm_rope(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 1, 64, 1e-6f, 0,
+                        WA_BF16, nullptr) == WA_OK);
+  CHECK(wa_qk_norm_rope(q, k, o, o, f, f, nullptr, nullptr, 4, 1, 64, 1e-6f, 0, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_qk_norm_rope(q, k, q, k, f, f, nullptr, nullptr, 4, 1, 64, -1.f, 0, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_qk_norm_rope(q, k, q, k, f, f, nullptr, nullptr, 4, 1, 64, 1e-6f, 8, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_qk_norm_rope(q, k, q, k, f, f, nullptr, nullptr, 4, 1, 48, 1e-6f, 0, WA_BF16, nullptr) ==
+        WA_ERR_UNSUPPORTED);
+}
+
+// Threads creating, fetching, introspecting and releasing plans of six geometries at once
+// (more than the cache holds, so evictions race with fetches).
+static void threads(int n) {
+  std::vector<std::thread> ts;
+  for (int t = 0; t < n; ++t)
+    ts.emplace_back([t] {
+      for (int i = 0; i < 40; ++i) {
+        const int g = (t + i) % 6;
+        wa_plan* p = nullptr;
+        if (wa_plan_create(20 + g, 6, g, 2, 1, 2, 64, &p) != WA_OK || !p) std::abort();
+        wa_plan_info_t info;
+        if (wa_plan_info(p, &info) != WA_OK || info.T != 20 + g) std::abort();
+        std::vector<int32_t> groups(size_t(info.n_groups) * 6);
+        if (wa_plan_groups(p, groups.data(), groups.size()) != WA_OK) std::abort();
+        if (wa_plan_release(p) != WA_OK) std::abort();
+      }
+    });
+  for (auto& th : ts) th.join();
+  g_checks += n * 40;
+}
+
+int main(int argc, char** argv) {
+  const int n_threads = argc > 1 ? std::atoi(argv[1]) : 0;
+  if (n_threads > 0) {
+    threads(n_threads);
+  } else {
+    sweep();
+    cache();
+    errors();
+    threads(4);
+  }
+  std::printf("OK %ld\n", g_checks);
+  std::fflush(stdout);
+  return 0;
+}

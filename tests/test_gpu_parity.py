@@ -12,9 +12,11 @@ import numpy as np
 import pytest
 import torch
 
+from _oracle_pool import by_heads
+from _oracle_pool import workers as by_heads_workers
 from chunk_windowed_softmax_amd.workloads import WORKLOADS, make_custom_inputs, make_inputs
-from oracle import (Geometry, causal_attention_reference, causal_attention_rows, window_attention_reference,
-                    window_attention_rows)
+from oracle import (Geometry, causal_attention_reference, chunk_span_rows, plan_groups,
+                    window_attention_reference, window_attention_rows, window_bounds)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,63 +43,50 @@ def _run(wa, w, q, k, v, out=None):
     return o
 
 
-@pytest.mark.parametrize("name", ["tiny", "small", "dense"])
+@pytest.mark.parametrize("name", ["tiny", "small", "dense", "ragged", "h3"])
 def test_full_parity(gpu_lib, name):
+    """Every row and head of the workload against the fp64 oracle (per-frame loop)."""
     w = WORKLOADS[name]
     _say(f"full parity {name}: T={w.T} S={w.S} G={w.G} K={w.K} r={w.radius} H={w.H} d={w.d} {w.dtype}")
     q, k, v = make_inputs(w, seed=0)
-    ref = window_attention_reference(q, k, v, Geometry(*w.geometry))
     out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda())
     assert out.dtype == w.dtype and tuple(out.shape) == (w.L, w.H, w.d)
-    rel, mx = _errors(out.float().cpu(), ref)
+    out = out.float().cpu()
+    _say(f"{name}: oracle on all {w.L} rows x {w.H} heads ({by_heads_workers()} threads)")
+    ref = by_heads(window_attention_reference, q, k, v, Geometry(*w.geometry))
+    rel, mx = _errors(out, ref)
     _say(f"{name}: rel_l2={rel:.3e} max_abs={mx:.3e}")
     assert rel <= REL_L2 and mx <= MAX_ABS
 
 
-def test_ragged_parity(gpu_lib):
-    w = WORKLOADS["ragged"]
-    _say("ragged parity (heads 0, 7, 15 in full; all heads on sampled rows)")
-    q, k, v = make_inputs(w, seed=0)
-    out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda()).float().cpu()
-    heads = [0, 7, 15]
-    ref = window_attention_reference(q[:, heads], k[:, heads], v[:, heads], Geometry(*w.geometry))
-    rel, mx = _errors(out[:, heads], ref)
-    _say(f"ragged heads {heads}: rel_l2={rel:.3e} max_abs={mx:.3e}")
-    assert rel <= REL_L2 and mx <= MAX_ABS
-    rng = np.random.default_rng(1)
-    rows = np.unique(np.concatenate([rng.choice(w.L, 48, replace=False), [0, w.T * w.S - 1, w.T * w.S, w.L - 1]]))
-    ref_rows = window_attention_rows(q, k, v, Geometry(*w.geometry), rows, range(w.H))
-    rel, mx = _errors(out[rows], ref_rows)
-    _say(f"ragged sampled rows: rel_l2={rel:.3e} max_abs={mx:.3e}")
-    assert rel <= REL_L2 and mx <= MAX_ABS
-
-
-def _sample_rows(w, n, seed):
+def _h3_rows(w, n_random, seed):
+    """Rows of every window group's first and last 256-row item (first and last row of
+    each), of every 256-row global tile (first and last row), and `n_random` more."""
+    geom = Geometry(*w.geometry)
+    rows = []
+    for g in plan_groups(geom):
+        last = g.q_begin + (g.q_end - 1 - g.q_begin) // 256 * 256
+        rows += [g.q_begin, min(g.q_end, g.q_begin + 256) - 1, last, g.q_end - 1]
+    for r0 in range(geom.n_frame_rows, geom.L, 256):
+        rows += [r0, min(geom.L, r0 + 256) - 1]
     rng = np.random.default_rng(seed)
-    n_frame = w.T * w.S
-    edges = [0, w.S - 1, n_frame - 1, n_frame, w.L - 1]
-    chunk_rows = w.K * w.S
-    edges += [c * chunk_rows for c in range(1, 4)] + [c * chunk_rows - 1 for c in range(1, 4)]
-    picks = rng.choice(w.L, n, replace=False)
-    glob = n_frame + rng.choice(w.G, min(16, w.G), replace=False) if w.G else []
-    return np.unique(np.concatenate([picks, edges, glob]).astype(np.int64))
+    rows += rng.choice(w.L, n_random, replace=False).tolist()
+    return np.unique(np.asarray(rows, dtype=np.int64))
 
 
-@pytest.mark.parametrize("name", ["h3", "h3_full"])
-def test_h3_scale_sampled_parity(gpu_lib, name):
-    w = WORKLOADS[name]
-    _say(f"{name}: generating inputs L={w.L} H={w.H}")
+def test_h3_full_sampled_parity(gpu_lib):
+    """The 56-head H3 shape: every head, on rows at every group's item edges and every
+    global tile (the oracle's per-row form)."""
+    w = WORKLOADS["h3_full"]
+    _say(f"h3_full: generating inputs L={w.L} H={w.H}")
     q, k, v = make_inputs(w, seed=0)
-    _say(f"{name}: running")
-    out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda())
-    assert not torch.isnan(out).any()
-    out = out.cpu()
-    rows = _sample_rows(w, 96 if w.H <= 8 else 24, seed=2)
-    heads = list(range(w.H)) if w.H <= 8 else [0, 13, 27, 41, 55]
-    _say(f"{name}: oracle on {len(rows)} rows x {len(heads)} heads")
-    ref = window_attention_rows(q, k, v, Geometry(*w.geometry), rows, heads)
-    rel, mx = _errors(out[rows][:, heads].float(), ref)
-    _say(f"{name} sampled: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    _say("h3_full: running")
+    out = _run(gpu_lib, w, q.cuda(), k.cuda(), v.cuda()).cpu()
+    rows = _h3_rows(w, 16, seed=2)
+    _say(f"h3_full: oracle on {len(rows)} rows x {w.H} heads")
+    ref = by_heads(window_attention_rows, q, k, v, Geometry(*w.geometry), rows, [0])
+    rel, mx = _errors(out[rows].float(), ref)
+    _say(f"h3_full sampled: rel_l2={rel:.3e} max_abs={mx:.3e}")
     assert rel <= REL_L2 and mx <= MAX_ABS
 
 
@@ -125,30 +114,93 @@ def test_edge_geometries(gpu_lib, geom, H, d, dtype):
     assert rel <= REL_L2 and mx <= MAX_ABS
 
 
-def test_cover_determinism_locality(gpu_lib):
-    """Every output element written (NaN prefill), bitwise repeatable, and keys outside a
-    row's window are never read (perturbing them leaves those rows bit-identical)."""
-    w = WORKLOADS["small"]
-    _say("cover / determinism / locality on small")
+def _persistent(plan, H):
+    """Whether wa_forward takes the persistent work-queue launch for this plan: it does
+    when the plan has more than two (head, item) units per compute unit."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    return plan.info["n_items"] * H > 2 * cus
+
+
+@pytest.mark.parametrize("name", ["tiny", "small", "dense", "ragged", "h3", "h3_full"])
+def test_cover_determinism_locality(gpu_lib, name):
+    """Every output element written (NaN prefill), bitwise repeatable over three calls in a
+    row (on the persistent launch these reuse the work-queue counters the previous call
+    reset), and keys outside a row's window never read: perturbing the frame rows after
+    chunk 0's window leaves chunk 0's rows bit-identical, and perturbing the rows before the
+    last chunk's window leaves the last chunk's rows bit-identical."""
+    w = WORKLOADS[name]
+    geom = Geometry(*w.geometry)
+    _say(f"cover / determinism / locality on {name}")
     q, k, v = (x.cuda() for x in make_inputs(w, seed=4))
     plan = gpu_lib.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
-    out1 = torch.full_like(q, float("nan"))
-    gpu_lib.wa_forward(plan, q, k, v, out=out1)
-    out2 = torch.full_like(q, float("nan"))
-    gpu_lib.wa_forward(plan, q, k, v, out=out2)
+    if name in ("ragged", "h3", "h3_full"):
+        assert _persistent(plan, w.H), "expected the persistent work-queue launch"
+    outs = []
+    for _ in range(3):
+        o = torch.full_like(q, float("nan"))
+        gpu_lib.wa_forward(plan, q, k, v, out=o)
+        outs.append(o)
     torch.cuda.synchronize()
-    assert not torch.isnan(out1).any()
-    assert torch.equal(out1, out2)
-    # chunk 0 (frames 0..2) sees chunks 0..1 = rows [0, 1536) plus globals
-    span_end = 2 * w.K * w.S
-    k2, v2 = k.clone(), v.clone()
-    k2[span_end:w.T * w.S] = 7.0
-    v2[span_end:w.T * w.S] = -7.0
-    out3 = gpu_lib.wa_forward(plan, q, k2, v2)
+    assert not torch.isnan(outs[0]).any()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    ref = outs[0]
+    del outs
+    n_frame, C = geom.n_frame_rows, geom.n_chunks
+    _, first_end = chunk_span_rows(geom, 0, 0)
+    _, span_end = chunk_span_rows(geom, *window_bounds(geom, 0))
+    last_begin, _ = chunk_span_rows(geom, C - 1, C - 1)
+    span_begin, _ = chunk_span_rows(geom, *window_bounds(geom, (C - 1) * geom.K))
+    if span_end == n_frame:
+        assert name in ("tiny", "dense") or w.radius >= C - 1
+    else:
+        k2, v2 = k.clone(), v.clone()
+        k2[span_end:n_frame] = 7.0
+        v2[span_end:n_frame] = -7.0
+        out3 = gpu_lib.wa_forward(plan, q, k2, v2)
+        torch.cuda.synchronize()
+        assert torch.equal(out3[:first_end], ref[:first_end])
+        assert not torch.equal(out3[first_end:n_frame], ref[first_end:n_frame])
+        del k2, v2, out3
+    if span_begin > 0:
+        k2, v2 = k.clone(), v.clone()
+        k2[:span_begin] = -6.0
+        v2[:span_begin] = 5.0
+        out3 = gpu_lib.wa_forward(plan, q, k2, v2)
+        torch.cuda.synchronize()
+        assert torch.equal(out3[last_begin:n_frame], ref[last_begin:n_frame])
+        assert not torch.equal(out3[:last_begin], ref[:last_begin])
+
+
+def test_shared_plan_on_two_streams(gpu_lib):
+    """Two handles of one geometry (one cached plan, one set of queue counters and
+    workspace) used on two streams with no synchronisation in between: the library orders
+    the calls, so both results equal the ones computed one after the other."""
+    w = WORKLOADS["ragged"]
+    _say("shared plan on two streams (ragged)")
+    q, k, v = (x.cuda() for x in make_inputs(w, seed=11))
+    q2 = torch.flip(q, dims=[0]).contiguous()
+    p1 = gpu_lib.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
+    p2 = gpu_lib.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
+    assert _persistent(p1, w.H)
+    ref1 = gpu_lib.wa_forward(p1, q, k, v)
+    ref2 = gpu_lib.wa_forward(p1, q2, k, v)
     torch.cuda.synchronize()
-    first_chunk = w.K * w.S
-    assert torch.equal(out3[:first_chunk], out1[:first_chunk])
-    assert not torch.equal(out3[first_chunk:2 * first_chunk], out1[first_chunk:2 * first_chunk])
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for rep in range(3):
+        o1 = torch.full_like(q, float("nan"))
+        o2 = torch.full_like(q, float("nan"))
+        torch.cuda.synchronize()
+        gpu_lib.wa_forward(p1, q, k, v, out=o1, stream=s1)
+        gpu_lib.wa_forward(p2, q2, k, v, out=o2, stream=s2)
+        gpu_lib.wa_forward(p2, q, k, v, out=o1, stream=s1)
+        outs.append((o1, o2))
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        assert torch.equal(o1, ref1)
+        assert torch.equal(o2, ref2)
 
 
 def test_rows_sum_to_one_and_fp32_output(gpu_lib):
@@ -180,7 +232,8 @@ def test_score_jump_parity(gpu_lib):
     _hot_key(q, k, T * S + 10, 700, 10.0)  # global row
     _hot_key(q, k, 300, 1030, 12.0)      # window row, hot key among the global keys
     plan = gpu_lib.wa_plan_create(T, S, G, K, r, H, d)
-    out = gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda())
+    out = torch.full((L, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda(), out=out)
     torch.cuda.synchronize()
     ref = window_attention_reference(q, k, v, Geometry(T, S, G, K, r))
     got = out.float().cpu()
@@ -234,39 +287,49 @@ def test_causal_parity(gpu_lib, n, H, d, dtype):
     assert rel <= REL_L2 and mx <= MAX_ABS
 
 
-def test_audio_causal_sampled_parity(gpu_lib):
+def test_audio_causal_full_parity(gpu_lib):
+    """The audio_causal workload (persistent launch) in full against the fp64 causal oracle."""
     w = WORKLOADS["audio_causal"]
     _say(f"audio_causal: L={w.L} H={w.H} d={w.d} fp32")
     q, k, v = make_inputs(w, seed=0)
     plan = gpu_lib.wa_causal_plan_create(w.L, w.H, w.d)
-    out = gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda())
+    out = torch.full((w.L, w.H, w.d), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda(), out=out)
     torch.cuda.synchronize()
     out = out.cpu()
-    assert out.dtype == torch.float32 and not torch.isnan(out).any()
-    rng = np.random.default_rng(7)
-    edges = [0, 1, 31, 32, 63, 64, 65, 255, 256, 257, 4095, 4096, w.L - 2, w.L - 1]
-    rows = np.unique(np.concatenate([rng.choice(w.L, 48, replace=False), edges]).astype(np.int64))
-    _say(f"audio_causal: oracle on {len(rows)} rows x {w.H} heads")
-    ref = causal_attention_rows(q, k, v, rows, range(w.H))
-    rel, mx = _errors(out[rows].float(), ref)
-    _say(f"audio_causal sampled: rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert not torch.isnan(out).any()
+    _say(f"audio_causal: oracle on all rows x {w.H} heads ({by_heads_workers()} threads)")
+    ref = by_heads(causal_attention_reference, q, k, v)
+    rel, mx = _errors(out, ref)
+    _say(f"audio_causal: rel_l2={rel:.3e} max_abs={mx:.3e}")
     assert rel <= REL_L2 and mx <= MAX_ABS
 
 
-def test_causal_cover_determinism_and_no_future_keys(gpu_lib):
-    """NaN prefill is fully overwritten, results repeat bit for bit, and perturbing rows
-    >= j of k and v leaves output rows < j bit-identical (future keys are never used)."""
-    n, H, d = 700, 2, 64
-    _say("causal cover / determinism / future keys")
-    q, k, v = (x.cuda() for x in make_custom_inputs(n, H, d, torch.bfloat16, seed=8))
+@pytest.mark.parametrize("case", ["n700", "audio_causal"])
+def test_causal_cover_determinism_and_no_future_keys(gpu_lib, case):
+    """NaN prefill is fully overwritten, results repeat bit for bit over three calls, and
+    perturbing rows >= j of k and v leaves output rows < j bit-identical (future keys are
+    never used).  audio_causal takes the persistent work-queue launch."""
+    if case == "n700":
+        n, H, d, dtype, js = 700, 2, 64, torch.bfloat16, (1, 100, 256, 321, 699)
+        q, k, v = (x.cuda() for x in make_custom_inputs(n, H, d, dtype, seed=8))
+    else:
+        w = WORKLOADS["audio_causal"]
+        n, H, d, js = w.L, w.H, w.d, (1, 255, 4096, 10001, w.L - 1)
+        q, k, v = (x.cuda() for x in make_inputs(w, seed=8))
+    _say(f"causal cover / determinism / future keys: {case}")
     plan = gpu_lib.wa_causal_plan_create(n, H, d)
-    out1 = torch.full_like(q, float("nan"))
-    gpu_lib.wa_forward(plan, q, k, v, out=out1)
-    out2 = torch.full_like(q, float("nan"))
-    gpu_lib.wa_forward(plan, q, k, v, out=out2)
+    if case == "audio_causal":
+        assert _persistent(plan, H)
+    outs = []
+    for _ in range(3):
+        o = torch.full_like(q, float("nan"))
+        gpu_lib.wa_forward(plan, q, k, v, out=o)
+        outs.append(o)
     torch.cuda.synchronize()
-    assert not torch.isnan(out1).any() and torch.equal(out1, out2)
-    for j in (1, 100, 256, 321, 699):
+    out1 = outs[0]
+    assert not torch.isnan(out1).any() and torch.equal(out1, outs[1]) and torch.equal(out1, outs[2])
+    for j in js:
         k2, v2 = k.clone(), v.clone()
         k2[j:] = 3.0
         v2[j:] = -5.0

@@ -30,9 +30,21 @@ def _compile_asm(tmp_path, source="kernels.hip"):
     return out.read_text().split("\n")
 
 
+_LABEL = re.compile(r"(\.LBB\w+):")
+_BRANCH = re.compile(r"s_(?:branch|cbranch_\w+)\s+(\.LBB\w+)")
+
+
 def _sgpr_hazards(lines, window=8):
-    """(line, writer, load) for each buffer load whose descriptor SGPRs a vector
-    instruction wrote fewer than 5 wait states before it (within one basic block)."""
+    """(line, writer, load) for each buffer load whose descriptor or offset SGPRs a vector
+    instruction wrote fewer than 5 wait states before it, on any path into the load: the
+    scan walks back through the load's block and, at a block label, into every predecessor
+    (the fall-through block and every branch to the label), at most `window` instructions
+    deep on each path."""
+    branches = {}
+    for i, line in enumerate(lines):
+        b = _BRANCH.search(line)
+        if b:
+            branches.setdefault(b.group(1), []).append(i)
     found = []
     for i, line in enumerate(lines):
         m = re.search(r"buffer_load_dwordx4 \w+, s\[(\d+):(\d+)\], (\w+)", line)
@@ -42,31 +54,44 @@ def _sgpr_hazards(lines, window=8):
         so = re.match(r"s(\d+)$", m.group(3))  # the scalar offset, when it is a register
         if so:
             regs.add(int(so.group(1)))
-        waits, seen, j = 0, 0, i - 1
-        while j >= 0 and seen < window and waits < 5:
-            t = lines[j].strip()
-            j -= 1
-            if not t or t.startswith(";"):
-                continue
-            if t.startswith("."):
-                if t.startswith(".LBB"):
+        stack, visited = [(i - 1, 0, 0)], set()
+        while stack:
+            j, waits, seen = stack.pop()
+            while j >= 0 and seen < window and waits < 5:
+                t = lines[j].strip()
+                if not t or t.startswith(";"):
+                    j -= 1
+                    continue
+                lab = _LABEL.match(t)
+                if lab:  # also enter every block that branches here
+                    for src in branches.get(lab.group(1), []):
+                        if (src, waits, seen) not in visited:
+                            visited.add((src, waits, seen))
+                            stack.append((src, waits, seen))
+                    j -= 1
+                    continue
+                if t.startswith("."):
+                    j -= 1
+                    continue
+                if t.startswith("s_endpgm"):
                     break
-                continue
-            seen += 1
-            nop = re.match(r"s_nop (\d+)", t)
-            if nop:
-                waits += int(nop.group(1)) + 1
-                continue
-            if t.split()[0].startswith("v_") and len(t.split()) > 1:
-                dst = t.split()[1].rstrip(",")
-                d = re.match(r"s\[(\d+):(\d+)\]$", dst) or re.match(r"s(\d+)$", dst)
-                if d:
-                    lo = int(d.group(1))
-                    hi = int(d.group(2)) if d.re.groups > 1 else lo
-                    if regs & set(range(lo, hi + 1)):
-                        found.append((i, t, line.strip()))
-            waits += 1
-    return found
+                seen += 1
+                nop = re.match(r"s_nop (\d+)", t)
+                if nop:
+                    waits += int(nop.group(1)) + 1
+                    j -= 1
+                    continue
+                if t.split()[0].startswith("v_") and len(t.split()) > 1:
+                    dst = t.split()[1].rstrip(",")
+                    d = re.match(r"s\[(\d+):(\d+)\]$", dst) or re.match(r"s(\d+)$", dst)
+                    if d:
+                        lo = int(d.group(1))
+                        hi = int(d.group(2)) if d.re.groups > 1 else lo
+                        if regs & set(range(lo, hi + 1)):
+                            found.append((i, t, line.strip()))
+                waits += 1
+                j -= 1
+    return sorted(set(found))
 
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not available")
@@ -87,3 +112,14 @@ def test_hazard_scan_finds_a_planted_case():
     # the scalar offset register is checked too
     lines = ["\tv_readlane_b32 s12, v255, 3", "\ts_nop 0", "\tbuffer_load_dwordx4 v0, s[44:47], s12 offen lds"]
     assert len(_sgpr_hazards(lines)) == 1
+    # a writer in a predecessor block: reached by falling through a label ...
+    lines = ["\tv_readfirstlane_b32 s46, v2", ".LBB0_3:", "\ts_nop 0",
+             "\tbuffer_load_dwordx4 v0, s[44:47], 0 offen lds"]
+    assert len(_sgpr_hazards(lines)) == 1
+    # ... or by a branch to it from elsewhere (here a loop back edge after the load)
+    lines = ["\ts_mov_b32 s46, 0", "\ts_nop 7", ".LBB0_3:", "\ts_nop 0",
+             "\tbuffer_load_dwordx4 v0, s[44:47], 0 offen lds", "\ts_nop 7", "\tv_readfirstlane_b32 s46, v2",
+             "\ts_cbranch_scc1 .LBB0_3"]
+    assert len(_sgpr_hazards(lines)) == 1
+    lines.insert(7, "\ts_nop 4")
+    assert _sgpr_hazards(lines) == []
