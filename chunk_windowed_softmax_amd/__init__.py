@@ -9,6 +9,7 @@ Functions carry the C names:
 * ``wa_plan_create(T, S, G, K, radius, H, d) -> Plan``
 * ``wa_causal_plan_create(n, H, d) -> Plan`` (causal dense attention, the audio VAE's)
 * ``wa_forward(plan, q, k, v, out=None) -> out``
+* ``wa_forward_noalloc(plan, q, k, v, out) -> out`` (same call; allocates nothing)
 * ``wa_forward_fp8(plan, q8, k8, v8, scale_q, scale_k, scale_v, out=None) -> out`` (e4m3 inputs)
 * ``wa_qk_norm_rope(q, k, cos, sin, wq=None, wk=None, ...) -> (q_out, k_out)`` (the prologue)
 * ``wa_plan_info / wa_plan_groups / wa_plan_kv_indices / wa_plan_items / wa_plan_launch_order /
@@ -44,6 +45,7 @@ EXPORTED_SYMBOLS = (
     "wa_plan_launch_order",
     "wa_qk_norm_rope",
     "wa_forward_fp8",
+    "wa_forward_noalloc",
     "wa_last_error",
 )
 
@@ -92,6 +94,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.wa_plan_items.argtypes = [P, i32p, ctypes.c_size_t]
     lib.wa_plan_launch_order.argtypes = [P, i32p, ctypes.c_size_t]
     lib.wa_forward_fp8.argtypes = [P, P, P, P, ctypes.c_float, ctypes.c_float, ctypes.c_float, P, P]
+    lib.wa_forward_noalloc.argtypes = [P, P, P, P, P, ctypes.c_int, P]
     lib.wa_qk_norm_rope.argtypes = [P] * 8 + [ctypes.c_int] * 3 + [ctypes.c_float] + [ctypes.c_int] * 2 + [P]
     lib.wa_last_error.argtypes = []
     lib.wa_last_error.restype = ctypes.c_char_p
@@ -203,6 +206,14 @@ def wa_forward(plan: Plan, q, k, v, out=None, stream=None):
     return _forward("wa_forward", plan, q, k, v, out, stream)
 
 
+def wa_forward_noalloc(plan: Plan, q, k, v, out, stream=None):
+    """wa_forward through the entry point that allocates nothing (its partial results and
+    tables live in the library's static per-GPU workspace); ``out`` must be given."""
+    if out is None:
+        raise ValueError("wa_forward_noalloc needs a preallocated out")
+    return _forward("wa_forward_noalloc", plan, q, k, v, out, stream)
+
+
 def _forward(entry: str, plan: Plan, q, k, v, out, stream):
     import torch
 
@@ -310,4 +321,5 @@ __all__ = [
     "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
     "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
     "wa_plan_launch_order", "wa_causal_plan_create", "wa_qk_norm_rope", "WA_ROPE_INTERLEAVED", "wa_forward_fp8",
+    "wa_forward_noalloc",
 ]

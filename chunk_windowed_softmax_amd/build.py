@@ -27,7 +27,7 @@ DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-m
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",
           "-I", os.path.join(os.path.dirname(PKG), "include")]
 
-SOURCES = ["kernels.hip", "prologue.hip", "attn_fp8.hip", "api.cpp", "plan.cpp"]
+SOURCES = ["kernels.hip", "prologue.hip", "attn_fp8.hip", "noalloc.hip", "api.cpp", "plan.cpp"]
 
 
 def _compile(src: str) -> str:

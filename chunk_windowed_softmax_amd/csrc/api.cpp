@@ -316,7 +316,7 @@ int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n) {
   return WA_OK;
 }
 
-// Argument checks of wa_forward.
+// Argument checks shared by wa_forward and wa_forward_noalloc.
 static int check_forward(const char* who, const wa_plan* plan, const void* q, const void* k, const void* v,
                          const void* out, int dtype) {
   if (!plan) return fail(WA_ERR_INVALID, std::string(who) + ": plan is NULL");
@@ -414,6 +414,45 @@ int wa_forward(const wa_plan* cplan, const void* q, const void* k, const void* v
     }
     return enqueue_forward("wa_forward", a, q, k, v, dtype, static_cast<char*>(r->staging), elems, stream);
   });
+}
+
+int wa_forward_noalloc(const wa_plan* cplan, const void* q, const void* k, const void* v, void* out, int dtype,
+                       void* stream_v) {
+  int st = check_forward("wa_forward_noalloc", cplan, q, k, v, out, dtype);
+  if (st != WA_OK) return st;
+  const wa_plan* plan = cplan;
+  const wa::HostPlan& h = plan->host;
+  const int64_t elems = int64_t(h.L) * h.geo.H * h.geo.d;
+  // workspace layout: table | partials | staging, each part at a 256-byte boundary
+  auto up256 = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t table_bytes = plan->table.size() * sizeof(int32_t);
+  const size_t part_off = up256(table_bytes);
+  const size_t staging_off = part_off + up256(size_t(h.partial_bytes));
+  const size_t need = staging_off + (dtype == WA_F32 ? size_t(3 * elems * 2) : 0);
+  if (need > wa::kStaticWorkspaceBytes)
+    return fail(WA_ERR_UNSUPPORTED, "wa_forward_noalloc: this plan needs " + std::to_string(need) +
+                                        " bytes of workspace (tables, global-leg partials" +
+                                        (dtype == WA_F32 ? ", bf16 staging" : "") + "), above the static " +
+                                        std::to_string(wa::kStaticWorkspaceBytes) + " bytes");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward_noalloc: hipGetDevice: ") + hipGetErrorString(e));
+  void* ws = nullptr;
+  e = wa::static_workspace(dev, &ws);
+  if (e != hipSuccess)
+    return fail(WA_ERR_HIP, std::string("wa_forward_noalloc: static workspace address: ") + hipGetErrorString(e));
+  int n_cus = 0;
+  e = hipDeviceGetAttribute(&n_cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess || n_cus < 1) return fail(WA_ERR_HIP, "wa_forward_noalloc: hipDeviceGetAttribute failed");
+  char* base = static_cast<char*>(ws);
+  hipStream_t stream = static_cast<hipStream_t>(stream_v);
+  // The plan's tables, zeroed queue counters included, go into the workspace ahead of the
+  // kernels on the same stream (the workspace holds whatever the previous call left).
+  e = hipMemcpyAsync(base, plan->table.data(), table_bytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward_noalloc: table upload: ") + hipGetErrorString(e));
+  float* part = h.partial_bytes > 0 ? reinterpret_cast<float*>(base + part_off) : nullptr;
+  const wa::ForwardArgs a = forward_args(h, reinterpret_cast<int32_t*>(base), part, n_cus, out, dtype);
+  return enqueue_forward("wa_forward_noalloc", a, q, k, v, dtype, base + staging_off, elems, stream);
 }
 
 int wa_forward_fp8(const wa_plan* cplan, const void* q, const void* k, const void* v, float scale_q, float scale_k,

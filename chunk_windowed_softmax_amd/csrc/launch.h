@@ -34,6 +34,13 @@ struct ForwardArgs {
 // pass on `stream`.
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream);
 
+// Size of the static device workspace that wa_forward_noalloc uses (one per GPU).
+constexpr size_t kStaticWorkspaceBytes = size_t(128) << 20;
+
+// Device address of the static workspace on `device`, which must be the current device;
+// looked up once per device, then cached.
+hipError_t static_workspace(int device, void** ptr);
+
 // Enqueue an fp32 -> bf16 (round to nearest even) conversion of n elements (n % 4 == 0).
 hipError_t launch_f32_to_bf16(const float* src, void* dst, int64_t n, hipStream_t stream);
 

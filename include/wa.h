@@ -150,6 +150,31 @@ int wa_plan_release(wa_plan* plan);
 int wa_forward(const wa_plan* plan, const void* q, const void* k, const void* v, void* out,
                int dtype, void* stream);
 
+/* Bytes of the static device workspace of wa_forward_noalloc (one per GPU). */
+#define WA_STATIC_WORKSPACE_BYTES (128u << 20)
+
+/*
+ * wa_forward_noalloc -- wa_forward for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, result and errors as wa_forward, computed by the same kernels; but no
+ * call allocates anything, on the host or the device.  Instead of the plan's own device
+ * tables and workspace, every call uses one static workspace per GPU of
+ * WA_STATIC_WORKSPACE_BYTES (a device array that each GPU the library runs on holds until
+ * the process ends): the call enqueues, on `stream`, a copy of the plan's tables (work
+ * items, launch order, zeroed work-queue counters) from host memory that the plan owns
+ * into that workspace, then the kernels, which keep the global leg's partial results (and,
+ * for WA_F32, the bf16 copies of q, k, v) there too.  A plan whose tables, partials and
+ * staging need more than WA_STATIC_WORKSPACE_BYTES is rejected with WA_ERR_UNSUPPORTED
+ * (e.g. 56 heads of the H3-scale geometry; its 7-head share fits).
+ * Every call on one GPU shares that GPU's workspace, which keeps the last call's contents:
+ * calls that overlap on one GPU (on different streams, or from different threads without
+ * ordering) race and give wrong results; order them.  When the call is captured into a
+ * graph, the plan must outlive the graph (its tables are read at each launch).
+ */
+int wa_forward_noalloc(const wa_plan* plan, const void* q, const void* k, const void* v, void* out,
+                       int dtype, void* stream);
+
 /* wa_plan_info -- fill *info.  WA_ERR_INVALID for NULL arguments. */
 int wa_plan_info(const wa_plan* plan, wa_plan_info_t* info);
 

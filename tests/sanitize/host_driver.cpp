@@ -150,6 +150,19 @@ static void errors() {
   // Valid arguments reach the HIP runtime: with no device (or with the stub launchers of
   // this host-only build) the call fails with WA_ERR_HIP and a message, without a crash.
   CHECK(wa_forward(p, q, k, v, o, WA_BF16, nullptr) == WA_ERR_HIP && std::strlen(wa_last_error()) > 0);
+  CHECK(wa_forward_noalloc(nullptr, q, k, v, o, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward_noalloc(p, q, nullptr, v, o, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward_noalloc(p, q, k, v, o, 3, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward_noalloc(p, q, k, v, mem[1] + 32, WA_BF16, nullptr) == WA_ERR_INVALID);
+  CHECK(wa_forward_noalloc(p, q, k, v, o, WA_BF16, nullptr) == WA_ERR_HIP);
+  CHECK(wa_plan_release(p) == WA_OK);
+  // a plan beyond the static workspace (56 heads at the H3 scale) is rejected before any
+  // device call
+  CHECK(wa_plan_create(102, 960, 1024, 3, 1, 56, 128, &p) == WA_OK);
+  // addresses 2^40 bytes apart (never dereferenced), so the overlap check passes
+  auto far = [](uintptr_t i) { return reinterpret_cast<void*>((uintptr_t(1) << 40) * (i + 1)); };
+  CHECK(wa_forward_noalloc(p, far(0), far(1), far(2), far(3), WA_BF16, nullptr) == WA_ERR_UNSUPPORTED);
+  CHECK(std::strstr(wa_last_error(), "static") != nullptr);
   CHECK(wa_plan_release(p) == WA_OK);
   const float* f = reinterpret_cast<const float*>(mem[2]);
   CHECK(wa_qk_norm_rope(nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0, 1, 64, 1e-6f, 0,
