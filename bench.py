@@ -38,8 +38,10 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="h3",
                     help="workload name (h3, h3_full, small, ragged, dense, audio_causal, audio_causal_small)")
-    ap.add_argument("--op", default="attention", choices=["attention", "prologue", "fp8"],
-                    help="attention: wa_forward (default); prologue: wa_qk_norm_rope; fp8: wa_forward_fp8")
+    ap.add_argument("--op", default="attention", choices=["attention", "prologue", "fp8", "blocksparse"],
+                    help="attention: wa_forward (default); prologue: wa_qk_norm_rope; fp8: wa_forward_fp8; "
+                         "blocksparse: the block-sparse plan against the decomposed one")
+    ap.add_argument("--block", default="256x128", help="query x key block sizes for --op blocksparse")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip timing the CPU oracle")
     ap.add_argument("--cpu-heads", type=int, default=0,
                     help="heads of the workload the CPU oracle runs (0: all, at most 16)")
@@ -301,6 +303,87 @@ def bench_prologue(args, w) -> int:
     return 0
 
 
+def bench_blocksparse(args, w) -> int:
+    """The block-sparse plan (FlexAttention-style block mask, [VDN] §二) and the decomposed
+    plan on the same inputs, timed in alternating rounds in one process; the line reports the
+    block-sparse call and the A/B."""
+    import torch
+
+    import chunk_windowed_softmax_amd as wa
+    from chunk_windowed_softmax_amd.workloads import make_inputs
+
+    bq, bk = (int(x) for x in args.block.lower().split("x"))
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in make_inputs(w, seed=0))
+    out = torch.empty_like(q)
+    t0 = time.perf_counter()
+    plan_b = wa.wa_blocksparse_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d, bq, bk)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan_d = wa.wa_plan_create(w.T, w.S, w.G, w.K, w.radius, w.H, w.d)
+    info_b, info_d = plan_b.info, plan_d.info
+    flop = info_b["kept_pairs_per_head"] * w.H * 4 * w.d
+    stream = torch.cuda.current_stream(dev)
+    rounds = 4
+    calls_b, calls_d, walls = [], [], []
+    for r in range(rounds):
+        pc, ms = _time_calls(lambda: wa.wa_forward(plan_b, q, k, v, out=out, stream=stream),
+                             max(1, args.steps // rounds), args.warmup if r == 0 else 2, stream)
+        calls_b += pc
+        walls.append(ms)
+        pc, _ = _time_calls(lambda: wa.wa_forward(plan_d, q, k, v, out=out, stream=stream),
+                            max(1, args.steps // rounds), args.warmup if r == 0 else 2, stream)
+        calls_d += pc
+    steps = rounds * max(1, args.steps // rounds)
+    ms_step = statistics.fmean(walls)
+    mean_b, mean_d = statistics.fmean(calls_b), statistics.fmean(calls_d)
+    achieved = flop / (mean_b * 1e-3) / 1e12
+    res = {
+        "metric": f"kept-pair TFLOP/s of the block-sparse ({bq},{bk}) {w.name} call on 1 MI355X",
+        "value": round(flop / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == torch.bfloat16 else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"blocksparse {bq}x{bk} {w.name}", "T": w.T, "S": w.S, "G": w.G, "K": w.K,
+            "radius": w.radius, "H": w.H, "d": w.d, "L": w.L, "block_q": bq, "block_kv": bk,
+            "kept_pairs": info_b["kept_pairs_per_head"] * w.H, "flop_per_call": flop,
+            "parallelism": "single GPU",
+        },
+        "ms_per_call": {"median": round(statistics.median(calls_b), 4), "min": round(min(calls_b), 4),
+                        "mean": round(mean_b, 4)},
+        "plan_create_ms": round(plan_ms, 3),
+        "ab": {
+            "decomposed_ms_mean": round(mean_d, 4),
+            "blocksparse_ms_mean": round(mean_b, 4),
+            "blocksparse_time_over_decomposed": round(mean_b / mean_d, 4),
+            "computed_pairs_blocksparse": info_b["computed_pairs_per_head"] * w.H,
+            "computed_pairs_decomposed": info_d["computed_pairs_per_head"] * w.H,
+            "rounds": rounds,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_kernel (tile-list instantiation), then combine_kernel: one wa_forward call",
+            "duration": "mean HIP-event time of the timed block-sparse wa_forward calls, events recorded on "
+                        "the launch stream around each call (both kernels)",
+            "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "algorithmic_bytes": int(4 * w.L * w.H * w.d * q.element_size() + 2 * info_b["workspace_bytes"]),
+        },
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main() -> int:
     args = _parse()
     if args.gpus != 1:
@@ -322,6 +405,8 @@ def main() -> int:
         return bench_prologue(args, w)
     if args.op == "fp8":
         return bench_fp8(args, w)
+    if args.op == "blocksparse":
+        return bench_blocksparse(args, w)
     q_cpu, k_cpu, v_cpu = make_inputs(w, seed=0)
     dev = torch.device("cuda:0")
     q, k, v = (x.to(dev) for x in (q_cpu, k_cpu, v_cpu))

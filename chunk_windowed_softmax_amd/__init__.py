@@ -8,6 +8,7 @@ Functions carry the C names:
 
 * ``wa_plan_create(T, S, G, K, radius, H, d) -> Plan``
 * ``wa_causal_plan_create(n, H, d) -> Plan`` (causal dense attention, the audio VAE's)
+* ``wa_blocksparse_plan_create(T, S, G, K, radius, H, d, block_q, block_kv) -> Plan`` (block-sparse form)
 * ``wa_forward(plan, q, k, v, out=None) -> out``
 * ``wa_forward_noalloc(plan, q, k, v, out) -> out`` (same call; allocates nothing)
 * ``wa_forward_fp8(plan, q8, k8, v8, scale_q, scale_k, scale_v, out=None) -> out`` (e4m3 inputs)
@@ -36,6 +37,9 @@ WA_ITEM_COLS = 8
 EXPORTED_SYMBOLS = (
     "wa_plan_create",
     "wa_causal_plan_create",
+    "wa_blocksparse_plan_create",
+    "wa_plan_block_mask",
+    "wa_plan_tiles",
     "wa_plan_release",
     "wa_forward",
     "wa_plan_info",
@@ -64,6 +68,8 @@ class _PlanInfo(ctypes.Structure):
         ("block_m", ctypes.c_int32), ("block_n", ctypes.c_int32), ("n_splits", ctypes.c_int32),
         ("n_items", ctypes.c_int32), ("workspace_bytes", ctypes.c_int64),
         ("launch_xcds", ctypes.c_int32), ("launch_per_xcd", ctypes.c_int32), ("causal", ctypes.c_int32),
+        ("block_q", ctypes.c_int32), ("block_kv", ctypes.c_int32), ("n_qblocks", ctypes.c_int32),
+        ("n_kvblocks", ctypes.c_int32), ("n_tiles", ctypes.c_int32), ("computed_pairs_per_head", ctypes.c_int64),
     ]
 
 
@@ -86,6 +92,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     i32p = ctypes.POINTER(ctypes.c_int32)
     lib.wa_plan_create.argtypes = [ctypes.c_int] * 7 + [ctypes.POINTER(P)]
     lib.wa_causal_plan_create.argtypes = [ctypes.c_int] * 3 + [ctypes.POINTER(P)]
+    lib.wa_blocksparse_plan_create.argtypes = [ctypes.c_int] * 9 + [ctypes.POINTER(P)]
+    lib.wa_plan_block_mask.argtypes = [P, i32p, i32p, i32p, i32p, ctypes.c_size_t]
+    lib.wa_plan_tiles.argtypes = [P, i32p, ctypes.c_size_t]
     lib.wa_plan_release.argtypes = [P]
     lib.wa_forward.argtypes = [P, P, P, P, P, ctypes.c_int, P]
     lib.wa_plan_info.argtypes = [P, ctypes.POINTER(_PlanInfo)]
@@ -150,6 +159,35 @@ def wa_causal_plan_create(n: int, H: int, d: int) -> Plan:
     h = ctypes.c_void_p()
     _check(lib.wa_causal_plan_create(n, H, d, ctypes.byref(h)))
     return Plan(h)
+
+
+def wa_blocksparse_plan_create(T: int, S: int, G: int, K: int, radius: int, H: int, d: int, block_q: int,
+                               block_kv: int) -> Plan:
+    """Block-sparse plan of the window attention (block mask at (block_q, block_kv))."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check(lib.wa_blocksparse_plan_create(T, S, G, K, radius, H, d, block_q, block_kv, ctypes.byref(h)))
+    return Plan(h)
+
+
+def wa_plan_block_mask(plan: Plan):
+    """(kv_num_blocks, kv_indices, full_kv_num_blocks, full_kv_indices) of a block-sparse plan:
+    [n_qblocks], [n_qblocks, n_kvblocks] (unused entries -1), [n_qblocks], [n_qblocks, n_kvblocks]."""
+    nq, nk = plan.info["n_qblocks"], plan.info["n_kvblocks"]
+    kn, knp = _int32_buffer(nq)
+    fn, fnp = _int32_buffer(nq)
+    ki, kip = _int32_buffer(nq * nk)
+    fi, fip = _int32_buffer(nq * nk)
+    _check(load_library().wa_plan_block_mask(plan.handle, knp, kip, fnp, fip, nq * nk))
+    return kn[:nq], ki[:nq * nk].reshape(nq, nk), fn[:nq], fi[:nq * nk].reshape(nq, nk)
+
+
+def wa_plan_tiles(plan: Plan) -> np.ndarray:
+    """Tile-list entries of a block-sparse plan's items: (first key row << 1) | needs_mask."""
+    n = plan.info["n_tiles"]
+    arr, ptr = _int32_buffer(n)
+    _check(load_library().wa_plan_tiles(plan.handle, ptr, arr.size))
+    return arr[:n]
 
 
 def wa_plan_info(plan: Plan) -> dict:
@@ -321,5 +359,5 @@ __all__ = [
     "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
     "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
     "wa_plan_launch_order", "wa_causal_plan_create", "wa_qk_norm_rope", "WA_ROPE_INTERLEAVED", "wa_forward_fp8",
-    "wa_forward_noalloc",
+    "wa_forward_noalloc", "wa_blocksparse_plan_create", "wa_plan_block_mask", "wa_plan_tiles",
 ]

@@ -50,8 +50,9 @@ struct DeviceResources {
 
 struct wa_plan {
   wa::HostPlan host;
-  // Image of the plan's device tables as int32: the work items, the launch order, then
-  // kXcdCount + 1 zeroed work-queue counters (uploaded as one block).
+  // Image of the plan's device tables as int32: the work items, the launch order,
+  // kXcdCount + 1 zeroed work-queue counters, then the tile lists of a block-sparse plan
+  // (uploaded as one block).
   std::vector<int32_t> table;
   std::atomic<int> refs{1};
   std::atomic<bool> cached{true};
@@ -191,7 +192,9 @@ static int create_cached(const wa::Geometry& geo, wa_plan** out, const char* who
   wa::HostPlan hp;
   std::string err;
   const auto t0 = std::chrono::steady_clock::now();
-  const int st = geo.causal ? wa::build_causal_plan(geo.S, geo.H, geo.d, &hp, &err) : wa::build_plan(geo, &hp, &err);
+  const int st = geo.causal        ? wa::build_causal_plan(geo.S, geo.H, geo.d, &hp, &err)
+                 : geo.block_q > 0 ? wa::build_blocksparse_plan(geo, &hp, &err)
+                                   : wa::build_plan(geo, &hp, &err);
   if (st != 0) return fail(st, std::string(who) + ": " + err);
   log_plan(hp, std::chrono::duration<double, std::micro>(std::chrono::steady_clock::now() - t0).count());
   wa_plan* p = nullptr;
@@ -204,9 +207,11 @@ static int create_cached(const wa::Geometry& geo, wa_plan** out, const char* who
   {
     const wa::HostPlan& h = p->host;
     const size_t item_words = h.items.size() * (sizeof(wa::Item) / sizeof(int32_t));
-    p->table.assign(item_words + h.work.size() + (wa::kXcdCount + 1), 0);
+    const size_t tiles_at = item_words + h.work.size() + (wa::kXcdCount + 1);
+    p->table.assign(tiles_at + h.tiles.size(), 0);
     std::memcpy(p->table.data(), h.items.data(), item_words * sizeof(int32_t));
     std::memcpy(p->table.data() + item_words, h.work.data(), h.work.size() * sizeof(int32_t));
+    if (!h.tiles.empty()) std::memcpy(p->table.data() + tiles_at, h.tiles.data(), h.tiles.size() * sizeof(int32_t));
   }
   p->refs.store(2);  // the caller's handle + the cache's
   wa_plan* evicted = nullptr;
@@ -234,6 +239,16 @@ static int create_cached(const wa::Geometry& geo, wa_plan** out, const char* who
 
 int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan** out) {
   return create_cached(wa::Geometry{T, S, G, K, radius, H, d, 0}, out, "wa_plan_create");
+}
+
+int wa_blocksparse_plan_create(int T, int S, int G, int K, int radius, int H, int d, int block_q, int block_kv,
+                               wa_plan** out) {
+  if (block_q <= 0 || block_kv <= 0)
+    return fail(WA_ERR_INVALID, "wa_blocksparse_plan_create: block sizes must be positive");
+  wa::Geometry geo{T, S, G, K, radius, H, d, 0};
+  geo.block_q = block_q;
+  geo.block_kv = block_kv;
+  return create_cached(geo, out, "wa_blocksparse_plan_create");
 }
 
 int wa_causal_plan_create(int n, int H, int d, wa_plan** out) {
@@ -269,6 +284,35 @@ int wa_plan_info(const wa_plan* plan, wa_plan_info_t* info) {
   info->launch_xcds = wa::kXcdCount;
   info->launch_per_xcd = h.work_per_xcd;
   info->workspace_bytes = h.partial_bytes;
+  info->block_q = h.geo.block_q;
+  info->block_kv = h.geo.block_kv;
+  info->n_qblocks = h.n_qblocks;
+  info->n_kvblocks = h.n_kvblocks;
+  info->n_tiles = (int32_t)h.tiles.size();
+  info->computed_pairs_per_head = h.computed_pairs_per_head;
+  return WA_OK;
+}
+
+int wa_plan_block_mask(const wa_plan* plan, int32_t* kv_num_blocks, int32_t* kv_indices, int32_t* full_kv_num_blocks,
+                       int32_t* full_kv_indices, size_t n) {
+  if (!plan || !kv_num_blocks || !kv_indices || !full_kv_num_blocks || !full_kv_indices)
+    return fail(WA_ERR_INVALID, "wa_plan_block_mask: NULL argument");
+  const wa::HostPlan& h = plan->host;
+  if (h.geo.block_q <= 0) return fail(WA_ERR_INVALID, "wa_plan_block_mask: not a block-sparse plan");
+  const size_t nq = size_t(h.n_qblocks), nk = size_t(h.n_kvblocks);
+  if (n < nq * nk) return fail(WA_ERR_INVALID, "wa_plan_block_mask: destination too small");
+  std::memcpy(kv_num_blocks, h.kv_num.data(), nq * sizeof(int32_t));
+  std::memcpy(full_kv_num_blocks, h.full_num.data(), nq * sizeof(int32_t));
+  std::memcpy(kv_indices, h.kv_idx.data(), nq * nk * sizeof(int32_t));
+  std::memcpy(full_kv_indices, h.full_idx.data(), nq * nk * sizeof(int32_t));
+  return WA_OK;
+}
+
+int wa_plan_tiles(const wa_plan* plan, int32_t* dst, size_t n) {
+  if (!plan || !dst) return fail(WA_ERR_INVALID, "wa_plan_tiles: NULL argument");
+  const auto& tiles = plan->host.tiles;
+  if (n < tiles.size()) return fail(WA_ERR_INVALID, "wa_plan_tiles: destination too small");
+  if (!tiles.empty()) std::memcpy(dst, tiles.data(), tiles.size() * sizeof(int32_t));
   return WA_OK;
 }
 
@@ -360,6 +404,13 @@ static wa::ForwardArgs forward_args(const wa::HostPlan& h, int32_t* table, float
   a.part_o = part;
   a.part_ml = part ? part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;
   a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(h.geo.d)));
+  a.tile_list = h.geo.block_q > 0;
+  a.tiles = a.counters + (wa::kXcdCount + 1);
+  a.T = h.geo.T;
+  a.S = h.geo.S;
+  a.K = h.geo.K;
+  a.radius = h.geo.radius;
+  a.n_chunks = h.n_chunks;
   return a;
 }
 
@@ -467,6 +518,7 @@ int wa_forward_fp8(const wa_plan* cplan, const void* q, const void* k, const voi
   wa_plan* plan = const_cast<wa_plan*>(cplan);
   const wa::HostPlan& h = plan->host;
   if (h.geo.d != 128) return fail(WA_ERR_UNSUPPORTED, "wa_forward_fp8: head size must be 128");
+  if (h.geo.block_q > 0) return fail(WA_ERR_UNSUPPORTED, "wa_forward_fp8: block-sparse plans run through wa_forward");
   const int64_t elems = int64_t(h.L) * h.geo.H * h.geo.d;
   // out holds 2 bytes per element, the inputs 1
   auto hits = [&](const void* in) {

@@ -49,6 +49,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "launch.h"
 
@@ -71,6 +72,7 @@ constexpr int kBN = kBlockN;   // keys per tile
 static_assert(kBN == 64, "the fragment code below assumes 64-key tiles");
 
 constexpr int kXcds = kXcdCount;  // blocks are dispatched round-robin over the XCDs
+constexpr int kListOffset = 64;   // byte offset of a tile list in the output staging area
 
 // 16-byte chunk swizzle of an LDS row.  The LDS has 64 banks (256 bytes per pass); a
 // ds_read_b128 pass serves 16 lanes and a ds_read_tr16_b64 pass 32 lanes.
@@ -118,6 +120,13 @@ struct AttnParams {
   int H, G, frame_rows, n_items, total, per_xcd;
   uint32_t tensor_bytes;  // bytes of one of q/k/v: L * H * D * 2
   float scale_log2;
+};
+
+// Parameters of the tile-list instantiation (block-sparse plans): entries (first key row
+// << 1) | needs_mask, and the geometry whose window rule masks the flagged tiles.
+struct AttnParamsTL : AttnParams {
+  const int32_t* __restrict__ tiles;
+  int T, S, K, radius, n_chunks;
 };
 
 // Next work unit for a block on XCD `xcd`, run by one whole wave: its own XCD's queue first
@@ -168,9 +177,14 @@ constexpr int32_t kBufferWord3 = 0x00020000;
 // against the running max before the tile's own max is known; a wave-uniform slow path
 // redoes a block's tile when some weight exceeds 2^8, and for a unit's first tile and
 // tiles with masked keys (segment end, causal diagonal).
-template <int D, bool OUT_F32>
+//
+// TL (block-sparse plans): every item's keys are a list of 64-key tiles read through an
+// index list (copied into the idle output staging area of the LDS at the start of the unit);
+// flagged tiles take the slow path, which keeps each row's kept keys by the window rule of
+// the geometry (the row's chunk span and the global rows) instead of a segment end.
+template <int D, bool OUT_F32, bool TL>
 __global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void attn_kernel(AttnParams p) {
+void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   constexpr int CH = D / 8;                     // 16-byte chunks per row
   constexpr int ROWB = D * 2;                   // bytes per LDS row
   constexpr int TILEB = kBN * ROWB;             // bytes per K or V tile
@@ -185,6 +199,7 @@ void attn_kernel(AttnParams p) {
   constexpr int NBUF = 4;                       // LDS ring of (K, V) tile pairs
   constexpr int RINGB = NBUF * 2 * TILEB;       // bytes of the ring
   constexpr int STAGEB = 8192;                  // per-wave output staging area after the ring
+  static_assert(kListOffset + 4 * kMaxListTiles <= kNW * STAGEB, "a tile list fits the staging areas");
   __shared__ __attribute__((aligned(1024))) unsigned char smem[RINGB + kNW * STAGEB];  // K0 V0 K1 V1 ... stages
 
   const int tid = threadIdx.x;
@@ -259,10 +274,20 @@ void attn_kernel(AttnParams p) {
       }
   }
 
-  // ---- tile schedule: segment 0 then segment 1, 64 keys per tile
+  // ---- tile schedule: segment 0 then segment 1, 64 keys per tile (TL: the item's list)
   const int nt0 = (it.kv0_end - it.kv0_begin + kBN - 1) / kBN;
   const int nt1 = (it.kv1_end - it.kv1_begin + kBN - 1) / kBN;
-  const int nt = nt0 + nt1;
+  const int nt = TL ? it.kv0_end : nt0 + nt1;
+  // TL: the item's entries in LDS, past the unit slot of wave 0's staging area (the staging
+  // areas are idle until the output epilogue, and the loop reads its last entries before its
+  // last barrier, so no wave still reads them when another starts its epilogue)
+  int32_t* const list = reinterpret_cast<int32_t*>(smem + RINGB + kListOffset);
+  if constexpr (TL) {
+    for (int i = tid; i < nt; i += kNW * 64) list[i] = p.tiles[it.kv0_begin + i];
+    __syncthreads();
+  }
+  // entry of tile u (clamped to the last tile), a uniform LDS read
+  auto entry = [&](int u) __attribute__((always_inline)) -> int { return list[u < nt ? u : nt - 1]; };
   auto tile_range = [&](int t, int& n0, int& nend) __attribute__((always_inline)) {
     if (t < nt0) {
       n0 = it.kv0_begin + t * kBN;
@@ -278,9 +303,13 @@ void attn_kernel(AttnParams p) {
   // Rows past a segment end are the next rows of the tensor (finite data, masked out of the
   // softmax) or, past the tensor, zeros.
   auto tile_off = [&](int u) __attribute__((always_inline)) -> uint32_t {
-    int n0, nend;
-    tile_range(u < nt ? u : nt - 1, n0, nend);
-    return uint32_t(n0) * row_bytes;
+    if constexpr (TL) {
+      return uint32_t(entry(u) >> 1) * row_bytes;
+    } else {
+      int n0, nend;
+      tile_range(u < nt ? u : nt - 1, n0, nend);
+      return uint32_t(n0) * row_bytes;
+    }
   };
   // DMA load `idx` (slice idx / 2, K for even idx and V for odd) of the tile at row offset
   // `toff` into ring slot u % NBUF.
@@ -420,8 +449,34 @@ void attn_kernel(AttnParams p) {
   constexpr int NP = 4 * DB;                // matrix ops of a PV slot
   static_assert(NS % 4 == 0 && NP % 4 == 0 && (2 * KS) % NP == 0 && 16 % NP == 0 && NLD % 2 == 0,
                 "slot work must divide evenly over the steps");
-  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0) __attribute__((always_inline)) {
-    if (valid < kBN || causal) {
+  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool masked) __attribute__((always_inline)) {
+    if constexpr (TL) {
+      if (masked) {
+        // the window rule for this lane's query row: frame rows keep their window's chunk
+        // span and the global rows, global rows keep every key; keys past L are none
+        const int qrow = row0 + 32 * qb + l32;
+        int klo = 0, khi = p.frame_rows;
+        if (qrow < p.frame_rows) {
+          const int c = qrow / p.S / p.K;
+          const int lo = c - p.radius > 0 ? c - p.radius : 0;
+          const int hi = c + p.radius < p.n_chunks - 1 ? c + p.radius : p.n_chunks - 1;
+          const int fend = (hi + 1) * p.K < p.T ? (hi + 1) * p.K : p.T;
+          klo = lo * p.K * p.S;
+          khi = fend * p.S;
+        }
+        const int L = p.frame_rows + p.G;
+        // key (n0 + b*32 + (i/4)*8 + 4*hh + i%4) kept iff in [klo, khi) or in [frame_rows, L)
+        const int base = n0 + 4 * hh;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = base + b * 32 + (i >> 2) * 8 + (i & 3);
+            const bool keep = (j >= klo && j < khi) || (j >= p.frame_rows && j < L);
+            sa[b][i] = keep ? sa[b][i] : -__builtin_inff();
+          }
+      }
+    } else if (valid < kBN || causal) {
       // tile keys at or past `lim` are masked: the segment end, and for causal items also
       // every key after this lane's own query row
       int lim = valid;
@@ -512,10 +567,12 @@ void attn_kernel(AttnParams p) {
                  "v"(pw[qb][5]), "v"(pw[qb][6]), "v"(pw[qb][7]), "v"(pw[qb][8]), "v"(pw[qb][9]), "v"(pw[qb][10]),
                  "v"(pw[qb][11]), "v"(pw[qb][12]), "v"(pw[qb][13]), "v"(pw[qb][14]), "v"(pw[qb][15]));
   };
-  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool dirty) __attribute__((always_inline)) {
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool dirty, bool masked)
+                         __attribute__((always_inline)) {
     pin_p(qb);
     asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
-    if (dirty || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0) slow_block(qb, sa, valid, n0);
+    if (dirty || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
+      slow_block(qb, sa, valid, n0, masked);
     l_run[qb] += rs[qb][0] + rs[qb][1];
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -613,14 +670,27 @@ void attn_kernel(AttnParams p) {
   int valid_prev = kBN, n0_prev = 0;
   int nd = 0;                // next tile that takes the slow path
   bool dirty_prev = false;   // block 0's verdict on the previous tile (tile -1: none)
+  bool masked_prev = false;
   for (int t = 0; t < nt; ++t) {
     const uint32_t step_k = ring(t + 2) - ring(t + 1);  // slot advance after this tile's reads
     const uint32_t step_v = ring(t + 1) - ring(t);
-    int n0, nend;
-    tile_range(t, n0, nend);
-    const int valid = nend - n0;
-    const bool dirty = t == nd;
-    if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
+    int n0, valid;
+    bool dirty, masked;
+    int e_cur = 0, e_dma = 0;  // TL: entries of tile t and of tile t + 3 (read before the barrier)
+    if constexpr (TL) {
+      e_cur = entry(t);
+      e_dma = entry(t + 3);
+      n0 = 0;  // set from e_cur where first needed (after slot 2)
+      valid = kBN;
+      dirty = masked = false;
+    } else {
+      int nend;
+      tile_range(t, n0, nend);
+      valid = nend - n0;
+      dirty = t == nd;
+      if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
+      masked = false;  // (TL only: without tile lists the slow path masks by segment end)
+    }
 
     if (__builtin_expect(wave_active, 1)) {
       // slot 0
@@ -628,7 +698,7 @@ void attn_kernel(AttnParams p) {
         stage_at(1, s1, 8, NS, i);
         if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)), toff_a);
       });
-      check_block(1, s1, valid_prev, n0_prev, dirty_prev);
+      check_block(1, s1, valid_prev, n0_prev, dirty_prev, masked_prev);
       // slot 1
       rs[0][0] = rs[0][1] = 0.f;
       pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
@@ -642,15 +712,30 @@ void attn_kernel(AttnParams p) {
       for (int db = 0; db < DB; ++db) voff[db][0] += step_v, voff[db][1] += step_v;
       // slot 2
       s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
-      check_block(0, s0, valid, n0, dirty);
+      if constexpr (TL) {
+        const int e = __builtin_amdgcn_readfirstlane(e_cur);
+        n0 = e >> 1;
+        masked = (e & 1) != 0;
+        dirty = t == 0 || masked;
+      }
+      check_block(0, s0, valid, n0, dirty, masked);
     } else {
 #pragma unroll
       for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx, toff_a);
     }
 
+    if constexpr (TL) {
+      if (!wave_active) {  // the active waves set these before their slow-path check
+        const int e = __builtin_amdgcn_readfirstlane(e_cur);
+        n0 = e >> 1;
+        masked = (e & 1) != 0;
+        dirty = t == 0 || masked;
+      }
+    }
     WA_WAIT_VMCNT(NLD);  // tile t+1 has landed (tile t+2 may still be in flight) ...
     barrier();           // ... for every wave
-    toff_a = tile_off(t + 3);
+    if constexpr (TL) toff_a = uint32_t(e_dma >> 1) * row_bytes;
+    else toff_a = tile_off(t + 3);
 
     if (__builtin_expect(wave_active, 1)) {
       // slot 3 (after the last tile the K reads hit a buffer nobody uses)
@@ -672,11 +757,12 @@ void attn_kernel(AttnParams p) {
     valid_prev = valid;
     n0_prev = n0;
     dirty_prev = dirty;
+    masked_prev = masked;
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no DMA may still write this block's LDS at exit
   if (wave_active) {  // block 1 of the last tile
     s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { stage_at(1, s1, 8, NS, i); });
-    check_block(1, s1, valid_prev, n0_prev, dirty_prev);
+    check_block(1, s1, valid_prev, n0_prev, dirty_prev, masked_prev);
     pv_slot(1, true, [&](int) __attribute__((always_inline)) {});
   }
 #undef WA_WAIT_VMCNT
@@ -832,9 +918,9 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
   }
 }
 
-template <int D, bool OUT_F32>
+template <int D, bool OUT_F32, bool TL>
 hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
-  AttnParams p;
+  std::conditional_t<TL, AttnParamsTL, AttnParams> p;
   p.q = static_cast<const uint16_t*>(a.q);
   p.k = static_cast<const uint16_t*>(a.k);
   p.v = static_cast<const uint16_t*>(a.v);
@@ -853,8 +939,16 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   p.total = kXcds * a.work_per_xcd;
   p.scale_log2 = a.scale_log2;
   p.tensor_bytes = uint32_t(a.L) * uint32_t(a.H) * uint32_t(D * 2);
+  if constexpr (TL) {
+    p.tiles = a.tiles;
+    p.T = a.T;
+    p.S = a.S;
+    p.K = a.K;
+    p.radius = a.radius;
+    p.n_chunks = a.n_chunks;
+  }
   const int grid = a.grid;
-  hipLaunchKernelGGL((attn_kernel<D, OUT_F32>), dim3(grid), dim3(kNW * 64), 0, stream, p);
+  hipLaunchKernelGGL((attn_kernel<D, OUT_F32, TL>), dim3(grid), dim3(kNW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_splits > 1) {
@@ -869,8 +963,15 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
 
 hipError_t launch_forward(const ForwardArgs& a, hipStream_t stream) {
   if (a.block_m != kNW * kWaveRows) return hipErrorInvalidValue;
-  if (a.d == 128) return a.out_f32 ? launch_typed<128, true>(a, stream) : launch_typed<128, false>(a, stream);
-  if (a.d == 64) return a.out_f32 ? launch_typed<64, true>(a, stream) : launch_typed<64, false>(a, stream);
+  if (a.tile_list) {
+    if (a.d == 128)
+      return a.out_f32 ? launch_typed<128, true, true>(a, stream) : launch_typed<128, false, true>(a, stream);
+    if (a.d == 64) return a.out_f32 ? launch_typed<64, true, true>(a, stream) : launch_typed<64, false, true>(a, stream);
+    return hipErrorInvalidValue;
+  }
+  if (a.d == 128)
+    return a.out_f32 ? launch_typed<128, true, false>(a, stream) : launch_typed<128, false, false>(a, stream);
+  if (a.d == 64) return a.out_f32 ? launch_typed<64, true, false>(a, stream) : launch_typed<64, false, false>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -28,6 +28,12 @@ struct ForwardArgs {
   float* part_o;          // [n_splits, G, H, d] fp32
   float* part_ml;         // [n_splits, G, H, 2] fp32: running max (log2 units), row sum
   float scale_log2;       // log2(e) / sqrt(d)
+  // Block-sparse plans: every item is a list of 64-key tiles (kItemTileList) in `tiles`,
+  // entry = (first key row << 1) | needs_mask; masked tiles apply the window rule of the
+  // geometry below element by element.
+  bool tile_list;
+  const int32_t* tiles;
+  int T, S, K, radius, n_chunks;
 };
 
 // Enqueue the attention pass (both legs) and, when the global leg is split, the combine

@@ -16,9 +16,12 @@ namespace wa {
 struct Geometry {
   int T, S, G, K, radius, H, d;
   int causal = 0;  // 1: causal dense attention over S rows (T = 1, G = 0); see build_causal_plan
+  // > 0: block-sparse plan with query blocks of block_q rows and key blocks of block_kv
+  // keys (see build_blocksparse_plan)
+  int block_q = 0, block_kv = 0;
   bool operator==(const Geometry& o) const {
     return T == o.T && S == o.S && G == o.G && K == o.K && radius == o.radius && H == o.H && d == o.d &&
-           causal == o.causal;
+           causal == o.causal && block_q == o.block_q && block_kv == o.block_kv;
   }
 };
 
@@ -34,6 +37,9 @@ struct Item {  // one block_m-row query tile over up to two key segments (all he
   int32_t flags;     // kItemCausal: query row r sees keys <= r only
 };
 constexpr int32_t kItemCausal = 1;
+// The item's keys are a list of 64-key tiles (block-sparse plans): kv0_begin is the offset
+// of its first entry in HostPlan::tiles, kv0_end the number of entries.
+constexpr int32_t kItemTileList = 2;
 static_assert(sizeof(Item) == 32, "Item is uploaded as 8 int32");
 
 struct HostPlan {
@@ -52,6 +58,17 @@ struct HostPlan {
   // ones; blocks that empty their own queue take units from the other XCDs' queues.
   std::vector<int32_t> work;
   int32_t work_per_xcd = 0;
+  // Block-sparse plans only.  The block mask of the frame (window) rows in the layout of
+  // FlexAttention's BlockMask: for query block i (rows [i*block_q, min(T*S, (i+1)*block_q)))
+  // the key blocks with some but not all pairs kept (kv_num[i] entries of kv_idx row i) and
+  // those with every pair kept (full_num[i] entries of full_idx row i), ascending; rows are
+  // n_kvblocks long, unused entries -1.  Key block j covers keys [j*block_kv, (j+1)*block_kv)
+  // cut at L.
+  int32_t n_qblocks = 0, n_kvblocks = 0;
+  std::vector<int32_t> kv_num, kv_idx, full_num, full_idx;
+  // Tile lists of the items (kItemTileList): entry = (first key row << 1) | needs_mask.
+  std::vector<int32_t> tiles;
+  int64_t computed_pairs_per_head = 0;  // (query, key) pairs the work items compute, one head
 };
 
 constexpr int kBlockM = 256;  // query rows per work item: 4 waves x 64 rows
@@ -63,6 +80,9 @@ constexpr int kXcdCount = 8;  // MI355X: workgroups are dispatched round-robin o
 // longest window item (fewer partial results to merge).
 constexpr int kGlobalSplitDiv = 2;
 constexpr int kComputeUnits = 256;   // MI355X
+// Longest tile list of one item: the kernel keeps it in the 32 KB output staging area of the
+// LDS (four 8 KB wave areas) past a 64-byte slot.
+constexpr int kMaxListTiles = (4 * 8192 - 64) / 4;
 constexpr int kFineSplitRounds = 4;  // window units >= this many rounds of all compute units
 
 // Status codes mirror the C ABI (0 ok, 1 invalid, 2 unsupported).
@@ -71,6 +91,14 @@ int build_plan(const Geometry& g, HostPlan* out, std::string* err);
 // Causal dense attention over n rows (the audio VAE's attention): no groups, one leg of
 // block_m-row items, item rows [q0, q1) over keys [0, q1) with kItemCausal set.
 int build_causal_plan(int n, int H, int d, HostPlan* out, std::string* err);
+
+// Block-sparse (FlexAttention-style) plan of the same attention: the frame rows' block
+// mask at (block_q, block_kv) granularity and work items that run 256 query rows (one
+// query block of 256, or two of 128 over the union of their key blocks) over their key
+// blocks as 64-key tiles, masking the tiles of partially kept blocks element by element;
+// the global rows run the same split-KV leg as build_plan's, as tile lists.
+// block_q in {128, 256}, block_kv in {64, 128}.
+int build_blocksparse_plan(const Geometry& g, HostPlan* out, std::string* err);
 
 // Chunk window [lo, hi] of chunk c (clipped to existing chunks).
 inline void chunk_window(int c, int n_chunks, int radius, int* lo, int* hi) {

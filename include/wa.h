@@ -67,16 +67,23 @@ typedef struct wa_plan_info_t {
   int32_t launch_xcds;              /* launch order: number of XCD queues ... */
   int32_t launch_per_xcd;           /* ... and entries per queue (see wa_plan_launch_order) */
   int32_t causal;                   /* 1 for a wa_causal_plan_create plan */
+  int32_t block_q, block_kv;        /* block sizes of a block-sparse plan (0 otherwise) */
+  int32_t n_qblocks, n_kvblocks;    /* its block mask: query blocks x key blocks */
+  int32_t n_tiles;                  /* entries of wa_plan_tiles (0 without tile lists) */
+  int64_t computed_pairs_per_head;  /* (query, key) pairs the work items compute, one head:
+                                       rows x 64-key tiles, so at least kept_pairs_per_head */
 } wa_plan_info_t;
 
 /* Item flag bits (column WA_ITEM_FLAGS). */
 #define WA_ITEM_CAUSAL 1
+#define WA_ITEM_TILE_LIST 2 /* keys: a list of 64-key tiles (block-sparse plans, see below) */
 
 /* Columns of one row of wa_plan_items(). */
 enum {
   WA_ITEM_Q_BEGIN = 0, /* first query row of the item */
   WA_ITEM_Q_END,       /* one past the last query row (at most block_m rows) */
-  WA_ITEM_KV0_BEGIN,   /* first key segment [begin, end) */
+  WA_ITEM_KV0_BEGIN,   /* first key segment [begin, end); with WA_ITEM_TILE_LIST: first entry
+                          of the item's tiles in wa_plan_tiles, then the number of entries */
   WA_ITEM_KV0_END,
   WA_ITEM_KV1_BEGIN,   /* second key segment [begin, end); empty when begin == end */
   WA_ITEM_KV1_END,
@@ -118,6 +125,45 @@ int wa_plan_create(int T, int S, int G, int K, int radius, int H, int d, wa_plan
  * window groups (wa_plan_info reports n_groups = 0, causal = 1).
  */
 int wa_causal_plan_create(int n, int H, int d, wa_plan** out);
+
+/*
+ * wa_blocksparse_plan_create -- plan of the same window attention computed the
+ * block-sparse way, as the FlexAttention path of the lqnn.cn article on VDN-Minimax-H3 window
+ * attention does (§二: a block-level mask built from the window rule, computed at block
+ * granularity, so window edges are rounded up to whole blocks; §四 compares that path with
+ * the decomposed one).  The frame rows' block mask at (block_q, block_kv) granularity lists,
+ * for every query block, the key blocks with some kept pair; blocks kept in part are
+ * computed with the window rule applied element by element, blocks kept in full without
+ * it.  Work items are 256 query rows (one query block of 256, or two of 128 over the union of
+ * their key blocks) over their key blocks as 64-key tiles, read through an index list.  The
+ * global rows run the same split-KV leg as the wa_plan_create plan, so the two plans differ
+ * in the window leg only.  wa_forward with this plan returns the same attention (to rounding).
+ * block_q in {128, 256}, block_kv in {64, 128}; other arguments, cache and errors as
+ * wa_plan_create (the block sizes are part of the cache key).  wa_forward_fp8 rejects it.
+ */
+int wa_blocksparse_plan_create(int T, int S, int G, int K, int radius, int H, int d, int block_q,
+                               int block_kv, wa_plan** out);
+
+/*
+ * wa_plan_block_mask -- copy a block-sparse plan's block mask of the frame rows to host
+ * memory, in the layout of FlexAttention's BlockMask: query block i covers rows
+ * [i*block_q, min(T*S, (i+1)*block_q)), key block j keys [j*block_kv, min(L, (j+1)*block_kv)).
+ * kv_num_blocks[i] / kv_indices row i: the key blocks with some but not every pair kept;
+ * full_kv_num_blocks[i] / full_kv_indices row i: those with every pair kept (only whole
+ * blocks).  Indices ascending; each index row has n_kvblocks entries, unused ones -1.
+ * kv_num_blocks and full_kv_num_blocks hold n_qblocks entries; `n` is the capacity of each
+ * index array (at least n_qblocks * n_kvblocks).  WA_ERR_INVALID for other plans or a small n.
+ */
+int wa_plan_block_mask(const wa_plan* plan, int32_t* kv_num_blocks, int32_t* kv_indices,
+                       int32_t* full_kv_num_blocks, int32_t* full_kv_indices, size_t n);
+
+/*
+ * wa_plan_tiles -- copy the tile lists of a block-sparse plan's items to host memory (n_tiles
+ * int32; an item with WA_ITEM_TILE_LIST owns entries [KV0_BEGIN, KV0_BEGIN + KV0_END)): entry
+ * = (first key row << 1) | m, m = 1 when the tile's keys are masked element by element.
+ * WA_ERR_INVALID if n is too small.
+ */
+int wa_plan_tiles(const wa_plan* plan, int32_t* dst, size_t n);
 
 /*
  * wa_plan_release -- drop one reference.  The plan (and its device memory) is freed

@@ -29,6 +29,7 @@ from .qk_norm_rope import (  # noqa: F401
     rms_norm,
     rope,
 )
+from .block_mask import block_mask, block_mask_brute_force, block_sparse_computed_pairs  # noqa: F401
 from .fp8 import (  # noqa: F401
     decode_e4m3,
     fp8_causal_attention_reference,
