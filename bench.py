@@ -118,24 +118,24 @@ def recorded_traffic(workload: str, kernel: str = "attn_kernel"):
 
 
 def _time_calls(fn, steps: int, warmup: int, stream):
-    """Warm up, then time `steps` calls: HIP events on the launch stream around each call
-    and the wall clock around all of them (synchronised on both sides)."""
+    """Warm up, then time `steps` calls back to back: HIP events on the launch stream at the
+    start and the end of the timed region (no event between calls, so the host enqueues ahead
+    of the device) and the wall clock around it (synchronised on both sides).  Returns
+    (device ms per call, wall ms per call)."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    for i in range(steps):
-        starts[i].record(stream)
+    start.record(stream)
+    for _ in range(steps):
         fn()
-        ends[i].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return [s.elapsed_time(e) for s, e in zip(starts, ends)], wall * 1e3 / steps
+    return start.elapsed_time(end) / steps, wall * 1e3 / steps
 
 
 def _calibration_copy(x):
@@ -173,10 +173,10 @@ def bench_fp8(args, w) -> int:
     stream = torch.cuda.current_stream(dev)
     if args.calibration_copy:
         _calibration_copy(q8)
-    per_call, ms_step = _time_calls(lambda: wa.wa_forward_fp8(plan, q8, k8, v8, sq, sk, sv, out=out, stream=stream),
-                                    args.steps, args.warmup, stream)
+    dev_ms, ms_step = _time_calls(lambda: wa.wa_forward_fp8(plan, q8, k8, v8, sq, sk, sv, out=out, stream=stream),
+                                  args.steps, args.warmup, stream)
     value = flop / (ms_step * 1e-3) / 1e12
-    achieved = flop / (statistics.fmean(per_call) * 1e-3) / 1e12
+    achieved = flop / (dev_ms * 1e-3) / 1e12
     traffic, traffic_rec = recorded_traffic(w.name, "attn_fp8_kernel")
     res = {
         "metric": "kept-pair TFLOP/s of the FP8 (e4m3) window call at the H3-scale share on 1 MI355X",
@@ -196,14 +196,13 @@ def bench_fp8(args, w) -> int:
             "H": w.H, "d": w.d, "L": w.L, "kept_pairs": info["kept_pairs_per_head"] * w.H,
             "flop_per_call": flop, "scales": "per tensor", "parallelism": "single GPU",
         },
-        "ms_per_call": {"median": round(statistics.median(per_call), 4), "min": round(min(per_call), 4),
-                        "mean": round(statistics.fmean(per_call), 4)},
+        "ms_per_call": {"device_mean": round(dev_ms, 4)},
         "plan_create_ms": round(plan_ms, 3),
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_fp8_kernel, then its merge kernel when the global leg is split: one wa_forward_fp8 call",
-            "duration": "mean HIP-event time of the timed wa_forward_fp8 calls, events recorded on the launch "
-                        "stream around each call (both kernels)",
+            "duration": "device time of the timed region (HIP events on the launch stream before the first and "
+                        "after the last call) / calls: both kernels",
             "achieved": round(achieved, 2),
             "peak": MFMA_FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -243,11 +242,11 @@ def bench_prologue(args, w) -> int:
     def call():
         wa.wa_qk_norm_rope(q, k, cos, sin, wq, wk, q_out=q_out, k_out=k_out, stream=stream)
 
-    per_call, ms_step = _time_calls(call, args.steps, args.warmup, stream)
+    dev_ms, ms_step = _time_calls(call, args.steps, args.warmup, stream)
     elem = q.element_size()
     nbytes = prologue_bytes(w.L, w.H, w.d, elem, True)
     value = nbytes / (ms_step * 1e-3) / 1e9
-    achieved = nbytes / (statistics.fmean(per_call) * 1e-3) / 1e9
+    achieved = nbytes / (dev_ms * 1e-3) / 1e9
     traffic, traffic_rec = recorded_traffic(w.name, "qk_norm_rope_kernel")
     res = {
         "metric": "QK-RMSNorm + rotary prologue algorithmic HBM GB/s at the H3-scale window call on 1 MI355X",
@@ -266,12 +265,12 @@ def bench_prologue(args, w) -> int:
             "workload": f"qk_norm_rope on {w.name} q/k", "L": w.L, "H": w.H, "d": w.d, "weights": True,
             "pairs": "rotate-half", "bytes_per_call": nbytes, "parallelism": "single GPU",
         },
-        "ms_per_call": {"median": round(statistics.median(per_call), 5), "min": round(min(per_call), 5),
-                        "mean": round(statistics.fmean(per_call), 5)},
+        "ms_per_call": {"device_mean": round(dev_ms, 5)},
         "roofline": {
             "bound": "hbm",
             "kernel": "qk_norm_rope_kernel: one wa_qk_norm_rope call",
-            "duration": "mean HIP-event time of the timed calls, events recorded on the launch stream",
+            "duration": "device time of the timed region (HIP events on the launch stream before the first and "
+                        "after the last call) / calls",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -324,18 +323,18 @@ def bench_blocksparse(args, w) -> int:
     flop = info_b["kept_pairs_per_head"] * w.H * 4 * w.d
     stream = torch.cuda.current_stream(dev)
     rounds = 4
-    calls_b, calls_d, walls = [], [], []
+    call_b = wa.prepared_forward(plan_b, q, k, v, out, stream)
+    call_d = wa.prepared_forward(plan_d, q, k, v, out, stream)
+    dev_b, dev_d, walls = [], [], []
     for r in range(rounds):
-        pc, ms = _time_calls(lambda: wa.wa_forward(plan_b, q, k, v, out=out, stream=stream),
-                             max(1, args.steps // rounds), args.warmup if r == 0 else 2, stream)
-        calls_b += pc
+        d, ms = _time_calls(call_b, max(1, args.steps // rounds), args.warmup if r == 0 else 2, stream)
+        dev_b.append(d)
         walls.append(ms)
-        pc, _ = _time_calls(lambda: wa.wa_forward(plan_d, q, k, v, out=out, stream=stream),
-                            max(1, args.steps // rounds), args.warmup if r == 0 else 2, stream)
-        calls_d += pc
+        d, _ = _time_calls(call_d, max(1, args.steps // rounds), args.warmup if r == 0 else 2, stream)
+        dev_d.append(d)
     steps = rounds * max(1, args.steps // rounds)
     ms_step = statistics.fmean(walls)
-    mean_b, mean_d = statistics.fmean(calls_b), statistics.fmean(calls_d)
+    mean_b, mean_d = statistics.fmean(dev_b), statistics.fmean(dev_d)
     achieved = flop / (mean_b * 1e-3) / 1e12
     res = {
         "metric": f"kept-pair TFLOP/s of the block-sparse ({bq},{bk}) {w.name} call on 1 MI355X",
@@ -356,8 +355,7 @@ def bench_blocksparse(args, w) -> int:
             "kept_pairs": info_b["kept_pairs_per_head"] * w.H, "flop_per_call": flop,
             "parallelism": "single GPU",
         },
-        "ms_per_call": {"median": round(statistics.median(calls_b), 4), "min": round(min(calls_b), 4),
-                        "mean": round(mean_b, 4)},
+        "ms_per_call": {"device_mean": round(mean_b, 4), "device_min_round": round(min(dev_b), 4)},
         "plan_create_ms": round(plan_ms, 3),
         "ab": {
             "decomposed_ms_mean": round(mean_d, 4),
@@ -370,8 +368,8 @@ def bench_blocksparse(args, w) -> int:
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_kernel (tile-list instantiation), then combine_kernel: one wa_forward call",
-            "duration": "mean HIP-event time of the timed block-sparse wa_forward calls, events recorded on "
-                        "the launch stream around each call (both kernels)",
+            "duration": "device time of the timed block-sparse regions (HIP events on the launch stream before "
+                        "the first and after the last call of each round) / calls: both kernels",
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",
@@ -426,14 +424,10 @@ def main() -> int:
         # one read + one write of q.numel()*2 bytes per copy; profiled beside the attention
         _calibration_copy(q)
 
-    per_call, ms_step = _time_calls(lambda: wa.wa_forward(plan, q, k, v, out=out, stream=stream),
-                                    args.steps, args.warmup, stream)
-    ms_med = statistics.median(per_call)
-    ms_min = min(per_call)
-    ms_mean = statistics.fmean(per_call)
+    dev_ms, ms_step = _time_calls(wa.prepared_forward(plan, q, k, v, out, stream), args.steps, args.warmup, stream)
 
     value = flop / (ms_step * 1e-3) / 1e12
-    achieved = flop / (ms_mean * 1e-3) / 1e12
+    achieved = flop / (dev_ms * 1e-3) / 1e12
     # Algorithmic HBM bytes: q, k, v read once and out written once, plus the global leg's
     # fp32 partials (written once, read once by the merge).
     elem = 2 if w.dtype == torch.bfloat16 else 4
@@ -459,14 +453,14 @@ def main() -> int:
             "flop_per_call": flop, "n_groups": info["n_groups"], "n_splits": info["n_splits"],
             "parallelism": "single GPU",
         },
-        "ms_per_call": {"median": round(ms_med, 4), "min": round(ms_min, 4), "mean": round(ms_mean, 4)},
+        "ms_per_call": {"device_mean": round(dev_ms, 4)},
         "pct_of_bf16_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
         "plan_create_ms": round(plan_ms, 3),
         "roofline": {
             "bound": "mfma",
             "kernel": "attn_kernel, then combine_kernel when the global leg is split: one wa_forward call",
-            "duration": "mean HIP-event time of the timed wa_forward calls, events recorded on the launch "
-                        "stream around each call (both kernels)",
+            "duration": "device time of the timed region (HIP events on the launch stream before the first and "
+                        "after the last call) / calls: both kernels",
             "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s",

@@ -252,6 +252,25 @@ def wa_forward_noalloc(plan: Plan, q, k, v, out, stream=None):
     return _forward("wa_forward_noalloc", plan, q, k, v, out, stream)
 
 
+def prepared_forward(plan: Plan, q, k, v, out, stream=None, noalloc: bool = False):
+    """Check the arguments of ``wa_forward`` (or ``wa_forward_noalloc``) once and return a
+    callable that repeats the call on the same tensors and stream with no further Python
+    work than the C call (raises on a non-zero status)."""
+    import torch
+
+    _forward("wa_forward_noalloc" if noalloc else "wa_forward", plan, q, k, v, out, stream)  # validates, runs once
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    fn = getattr(load_library(), "wa_forward_noalloc" if noalloc else "wa_forward")
+    args = (plan.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+            WA_F32 if q.dtype == torch.float32 else WA_BF16, ctypes.c_void_p(stream.cuda_stream))
+
+    def call():
+        _check(fn(*args))
+
+    return call
+
+
 def _forward(entry: str, plan: Plan, q, k, v, out, stream):
     import torch
 
@@ -359,5 +378,5 @@ __all__ = [
     "EXPORTED_SYMBOLS", "LIB_PATH", "Plan", "WaError", "WA_BF16", "WA_F32", "load_library", "wa_forward",
     "wa_last_error", "wa_plan_create", "wa_plan_groups", "wa_plan_info", "wa_plan_items", "wa_plan_kv_indices",
     "wa_plan_launch_order", "wa_causal_plan_create", "wa_qk_norm_rope", "WA_ROPE_INTERLEAVED", "wa_forward_fp8",
-    "wa_forward_noalloc", "wa_blocksparse_plan_create", "wa_plan_block_mask", "wa_plan_tiles",
+    "wa_forward_noalloc", "wa_blocksparse_plan_create", "wa_plan_block_mask", "wa_plan_tiles", "prepared_forward",
 ]

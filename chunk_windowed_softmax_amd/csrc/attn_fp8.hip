@@ -327,29 +327,41 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(Fp8Args p) {
 }
 
 // Merge of the global leg's key splits (as for the bf16 path): for each (global row, head),
-// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s, in bf16.
-__global__ __launch_bounds__(64) void combine_fp8_kernel(const float* __restrict__ part_o,
-                                                         const float* __restrict__ part_ml, uint16_t* __restrict__ out,
-                                                         int G, int H, int n_splits, int frame_rows) {
-  const int gi = blockIdx.x / H, h = blockIdx.x % H;
-  const int64_t stride = int64_t(G) * H;
-  const int64_t slot0 = int64_t(gi) * H + h;
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s, in bf16.  A thread
+// merges four columns of one (row, head) with 16-byte loads; the 32 threads of a (row, head)
+// read each split's partial row as one contiguous piece.
+constexpr int kCombineThreads = 256;
+constexpr int kCombineSlots = kCombineThreads / (kD / 4);  // (row, head) slots per block
+__global__ __launch_bounds__(kCombineThreads) void combine_fp8_kernel(const float* __restrict__ part_o,
+                                                                      const float* __restrict__ part_ml,
+                                                                      uint16_t* __restrict__ out, int G, int H,
+                                                                      int n_splits, int frame_rows) {
+  const int64_t stride = int64_t(G) * H;  // slots per split
+  const int64_t slot = int64_t(blockIdx.x) * kCombineSlots + threadIdx.x / (kD / 4);  // global row * H + head
+  if (slot >= stride) return;
+  const int c4 = (threadIdx.x % (kD / 4)) * 4;
   float M = -__builtin_inff();
-  for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_ml[(s * stride + slot0) * 2]);
+  for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_ml[(s * stride + slot) * 2]);
   float den = 0.f;
+  float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 4
   for (int s = 0; s < n_splits; ++s) {
-    const float* ml = part_ml + (s * stride + slot0) * 2;
-    den += __builtin_amdgcn_exp2f(ml[0] - M) * ml[1];
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (s * stride + slot) * 2);
+    const float w = __builtin_amdgcn_exp2f(ml.x - M);
+    den += w * ml.y;
+    const float4 o = *reinterpret_cast<const float4*>(part_o + (s * stride + slot) * kD + c4);
+    num.x += w * o.x;
+    num.y += w * o.y;
+    num.z += w * o.z;
+    num.w += w * o.w;
   }
   const float inv = 1.f / den;
-  const int64_t orow = (int64_t(frame_rows + gi) * H + h) * kD;
-  for (int dv = threadIdx.x; dv < kD; dv += 64) {
-    float num = 0.f;
-    for (int s = 0; s < n_splits; ++s)
-      num += __builtin_amdgcn_exp2f(part_ml[(s * stride + slot0) * 2] - M) * part_o[(s * stride + slot0) * kD + dv];
-    const __bf16 b = (__bf16)(num * inv);
-    out[orow + dv] = __builtin_bit_cast(uint16_t, b);
-  }
+  const int64_t orow = (int64_t(frame_rows) * H + slot) * kD + c4;  // row frame_rows + slot / H, head slot % H
+  const __bf16 b0 = (__bf16)(num.x * inv), b1 = (__bf16)(num.y * inv), b2 = (__bf16)(num.z * inv),
+               b3 = (__bf16)(num.w * inv);
+  const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, b0)) | (uint32_t(__builtin_bit_cast(uint16_t, b1)) << 16);
+  const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, b2)) | (uint32_t(__builtin_bit_cast(uint16_t, b3)) << 16);
+  *reinterpret_cast<uint2*>(out + orow) = make_uint2(lo, hi);
 }
 
 }  // namespace
@@ -361,8 +373,9 @@ hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream) {
   hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(kThreads), 2 * kBufB, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits <= 1) return e;
-  hipLaunchKernelGGL(combine_fp8_kernel, dim3(a.G * a.H), dim3(64), 0, stream, a.part_o, a.part_ml,
-                     static_cast<uint16_t*>(a.out), a.G, a.H, a.n_splits, a.frame_rows);
+  hipLaunchKernelGGL(combine_fp8_kernel, dim3((a.G * a.H + kCombineSlots - 1) / kCombineSlots), dim3(kCombineThreads),
+                     0, stream, a.part_o, a.part_ml, static_cast<uint16_t*>(a.out), a.G, a.H, a.n_splits,
+                     a.frame_rows);
   return hipGetLastError();
 }
 

@@ -88,8 +88,9 @@ __device__ __forceinline__ int swz(int row) {
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-// s_waitcnt with vmcnt = 0 and the other counters left at their maximum.
+// s_waitcnt with vmcnt = 0 (lgkmcnt = 0) and the other counters left at their maximum.
 constexpr int kVmcnt0 = 0x0F70;
+constexpr int kLgkmcnt0 = 0xC07F;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -693,7 +694,10 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
     }
 
     if (__builtin_expect(wave_active, 1)) {
-      // slot 0
+      // slot 0.  The K fragments it reads were loaded in slot 3 of the previous tile, long
+      // done: one wait for all of them instead of one per matrix op.
+      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+      __builtin_amdgcn_sched_barrier(0);
       s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
         stage_at(1, s1, 8, NS, i);
         if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)), toff_a);
@@ -876,36 +880,41 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
 }
 
 // Merge the global leg's key splits: for each (global row, head), with m_s in log2 units,
-// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.  A thread merges four
+// columns of one (row, head) with 16-byte loads; the D / 4 threads of a (row, head) read
+// each split's partial row as one contiguous piece, and the (row, head) slots of a block are
+// adjacent in every split.
+constexpr int kCombineThreads = 256;
 template <int D, bool OUT_F32>
-__global__ __launch_bounds__(64) void combine_kernel(const float* __restrict__ part_o,
-                                                     const float* __restrict__ part_ml, void* __restrict__ out,
-                                                     int G, int H, int n_splits, int frame_rows) {
-  const int gi = blockIdx.x / H, h = blockIdx.x % H;
-  const int64_t stride = (int64_t)G * H;  // slots per split
-  const int64_t slot0 = (int64_t)gi * H + h;
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ part_o,
+                                                                  const float* __restrict__ part_ml,
+                                                                  void* __restrict__ out, int G, int H, int n_splits,
+                                                                  int frame_rows) {
+  constexpr int TPS = D / 4;                     // threads per (row, head)
+  constexpr int SPB = kCombineThreads / TPS;     // (row, head) slots per block
+  const int64_t slot = int64_t(blockIdx.x) * SPB + threadIdx.x / TPS;  // = global row * H + head
+  const int64_t stride = int64_t(G) * H;         // slots per split
+  if (slot >= stride) return;
+  const int c4 = (threadIdx.x % TPS) * 4;
   float M = -__builtin_inff();
-  for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_ml[(s * stride + slot0) * 2]);
+  for (int s = 0; s < n_splits; ++s) M = __builtin_fmaxf(M, part_ml[(s * stride + slot) * 2]);
   float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
   for (int s = 0; s < n_splits; ++s) {
-    const float* ml = part_ml + (s * stride + slot0) * 2;
-    den += fast_exp2(ml[0] - M) * ml[1];
+    const float2 ml = *reinterpret_cast<const float2*>(part_ml + (s * stride + slot) * 2);
+    const float w = fast_exp2(ml.x - M);
+    den += w * ml.y;
+    const f32x4 o = *reinterpret_cast<const f32x4*>(part_o + (s * stride + slot) * D + c4);
+    num += w * o;
   }
   const float inv = 1.f / den;
-  const int64_t orow = ((int64_t)(frame_rows + gi) * H + h) * D;
-  for (int dv = threadIdx.x; dv < D; dv += 64) {
-    float num = 0.f;
-    for (int s = 0; s < n_splits; ++s) {
-      const float w = fast_exp2(part_ml[(s * stride + slot0) * 2] - M);
-      num += w * part_o[(s * stride + slot0) * D + dv];
-    }
-    const float o = num * inv;
-    if constexpr (OUT_F32) {
-      reinterpret_cast<float*>(out)[orow + dv] = o;
-    } else {
-      const __bf16 b = (__bf16)o;
-      reinterpret_cast<uint16_t*>(out)[orow + dv] = __builtin_bit_cast(uint16_t, b);
-    }
+  const f32x4 r = num * inv;
+  const int64_t orow = (int64_t(frame_rows) * H + slot) * D + c4;  // row frame_rows + slot / H, head slot % H
+  if constexpr (OUT_F32) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(out) + orow) = r;
+  } else {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(out) + orow) = u32x2{pack_bf16x2(r[0], r[1]), pack_bf16x2(r[2], r[3])};
   }
 }
 
@@ -952,8 +961,9 @@ hipError_t launch_typed(const ForwardArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.n_splits > 1) {
-    hipLaunchKernelGGL((combine_kernel<D, OUT_F32>), dim3(a.G * a.H), dim3(64), 0, stream, a.part_o, a.part_ml,
-                       a.out, a.G, a.H, a.n_splits, a.frame_rows);
+    constexpr int spb = kCombineThreads / (D / 4);
+    hipLaunchKernelGGL((combine_kernel<D, OUT_F32>), dim3((a.G * a.H + spb - 1) / spb), dim3(kCombineThreads), 0,
+                       stream, a.part_o, a.part_ml, a.out, a.G, a.H, a.n_splits, a.frame_rows);
     e = hipGetLastError();
   }
   return e;
