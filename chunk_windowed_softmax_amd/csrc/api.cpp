@@ -529,28 +529,14 @@ int wa_forward_fp8(const wa_plan* cplan, const void* q, const void* k, const voi
   DeviceResources* r = nullptr;
   int st = device_resources(plan, &r);
   if (st != WA_OK) return st;
-  wa::Fp8Args a;
+  wa::ForwardArgs a = forward_args(h, reinterpret_cast<int32_t*>(r->items), r->part, r->n_cus, out, WA_BF16);
   a.q = q;
   a.k = k;
   a.v = v;
-  a.out = out;
-  a.items = r->items;
-  a.work = reinterpret_cast<const int32_t*>(r->items + h.items.size());
-  a.per_xcd = h.work_per_xcd;
-  a.n_items = (int)h.items.size();
-  a.H = h.geo.H;
-  a.G = h.geo.G;
-  a.L = h.L;
-  a.d = h.geo.d;
-  a.frame_rows = h.n_frame_rows;
-  a.n_splits = h.n_splits;
-  a.part_o = r->part;
-  a.part_ml = r->part ? r->part + int64_t(h.n_splits) * h.geo.G * h.geo.H * h.geo.d : nullptr;
   a.scale_log2 = float(1.4426950408889634 / std::sqrt(double(h.geo.d)) * double(scale_q) * double(scale_k));
-  a.scale_v = scale_v;
   const hipStream_t stream = static_cast<hipStream_t>(stream_v);
   return ordered_launch(plan, r, stream, "wa_forward_fp8", [&]() -> int {
-    hipError_t e = wa::launch_forward_fp8(a, stream);
+    hipError_t e = wa::launch_forward_fp8(a, scale_v, stream);
     if (e != hipSuccess) return fail(WA_ERR_HIP, std::string("wa_forward_fp8 launch: ") + hipGetErrorString(e));
     return WA_OK;
   });

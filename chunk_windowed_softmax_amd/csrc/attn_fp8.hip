@@ -1,110 +1,204 @@
 // FP8 (e4m3) variant of the decomposed window attention (gfx950).
 //
-// Same work items and output contract as attn_kernel (window items over their chunk span and
-// the global rows; global-leg items write fp32 partials that a combine pass merges), with q,
-// k and v given as OCP e4m3 codes plus one fp32 scale per tensor (value = code * scale).  The
-// lqnn.cn article's fastest H3 configurations run in FP8 (§四); it does not say which
-// operands of the attention do, so both products run on gfx950's fp8 matrix cores here:
+// Same work units, launch order and output contract as attn_kernel (window items over their
+// chunk span and the global rows; global-leg items write fp32 partials that a combine pass
+// merges), with q, k and v given as OCP e4m3 codes plus one fp32 scale per tensor (value =
+// code * scale).  The lqnn.cn article's fastest H3 configurations run in FP8 (§四); it does
+// not say which operands of the attention do, so both products run on gfx950's fp8 matrix
+// cores:
 //   S^T = K Q^T      v_mfma_f32_32x32x64_f8f6f4, A = K rows from LDS, B = the wave's Q rows
 //                    held in registers; the head dimension (128) is two k-steps of 64;
-//   O^T += V^T P^T   same instruction, once per 64-key half of a tile: B = P^T rounded to
-//                    e4m3 straight from the S^T accumulators, A = V^T gathered from the
-//                    row-major V tile with ds_read_b64_tr_b8 (LDS transpose read), in the
-//                    key order of P.
+//   O^T += V^T P^T   the same instruction, once per 32-row d-block over a whole 64-key tile:
+//                    B = P^T rounded to e4m3 straight from the S^T accumulators, A = V^T
+//                    gathered from the row-major V tile with ds_read_b64_tr_b8 (LDS
+//                    transpose read), in the key order of P;
+//   l += 1 P^T       the same instruction with an all-ones A: the row sums of exactly the
+//                    rounded weights that multiply V, accumulated in fp32 by the matrix
+//                    core, so the weights applied to V sum to one.
 // Both operands of one matrix op map lane half h, byte j to the same k index, so any
-// consistent key (or channel) order is correct; the order used makes P's bytes the S^T
-// accumulator elements in register order.
-// Softmax: online over the tiles in the log2 domain with a lazily raised running max (the
-// weights may reach 2^8 before it rises; see the loop); the row sum adds the fp32 weights.
-// Output: O * scale_v / rowsum, rounded to bf16.
+// consistent key order is correct; the one used makes P's bytes the S^T accumulator elements
+// in register order.
 //
-// Block = 4 waves of 32 query rows, half of one of the plan's 256-row items; two blocks per
-// CU (two waves per SIMD from different blocks, whose phases drift apart: 2.4% faster than
-// one 8-wave block per item).  Blocks follow the plan's XCD-aware launch order, the two
-// halves of an item on one XCD.  K/V tiles of 128 keys (16 KB each) are double-buffered in
-// LDS and filled by direct global->LDS loads issued at the start of the previous tile; one
-// barrier per tile (128-key tiles: 11% faster than 64-key ones, whose barriers came twice as
-// often).
-// Rows are stored with their 16-byte chunks swizzled by row, so that the K fragment reads
-// and the V transpose reads are free of bank conflicts.
+// The structure is attn_kernel's: persistent blocks of 4 waves (one per SIMD), 64 query rows
+// per wave as two 32-row blocks (qb), 64-key tiles streamed through a 4-deep LDS ring by
+// direct global->LDS loads issued three tiles ahead, and per tile four slots of matrix ops
+// (S of block 0, PV of block 1 for the previous tile, S of block 1, PV of block 0), each
+// interleaved one matrix op at a time with the softmax of the other block, the LDS reads of
+// the next fragments and the loads.  A matrix op here takes 64 cycles and the vector work of
+// four weights (FMA, exp2, e4m3 packing, max) slightly longer (v_exp_f32 issues in about 10
+// cycles), so one group of four weights rides beside each matrix op and the kernel is bound
+// by vector issue, not by the matrix pipe.
+// Softmax: online over the tiles in the log2 domain, weights against a lazily raised running
+// max (they may reach 2^8, exact in e4m3, whose largest finite value is 448, before it
+// rises).  A block's tile takes the wave-uniform slow path when some weight exceeds 2^8, and
+// on a unit's first tile and tiles with masked keys: tile max, per-row raise of the running
+// max, rescale, weights again.
+// Output: O * scale_v / l, rounded to bf16, through an LDS staging area as whole rows.
+// LDS rows hold the 128 bytes of a key; their 16-byte chunks are swizzled per row (on the
+// global side of the loads) so that the K fragment reads and the V transpose reads are free
+// of bank conflicts.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
+#include "attn_common.h"
 #include "launch.h"
 
 namespace wa {
 namespace {
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kD = 128;             // head size = bytes per fp8 row
-constexpr int kBN = 2 * kBlockN;    // keys per tile
-constexpr int kWaves = 4;           // waves per block (two blocks per CU)
-constexpr int kThreads = 64 * kWaves;
-constexpr int kRows = 32 * kWaves;  // query rows per block
-constexpr int kHalves = kBlockM / kRows;  // blocks per plan item
-static_assert(kHalves * kRows == kBlockM, "blocks split a plan item evenly");
-static_assert(kBN == 128, "a tile is two 64-key P^T operands");
-constexpr int kTileB = kBN * kD;  // bytes of one K (or V) tile
-constexpr int kBufB = 2 * kTileB;  // K then V
+constexpr int kD = 128;               // head size = bytes per e4m3 row
+constexpr int kNW = 4;                // waves per block, one per SIMD
+constexpr int kWaveRows = 64;         // query rows per wave (two 32-row blocks)
+constexpr int kBN = kBlockN;          // keys per tile
+static_assert(kBN == 64, "one P^T operand covers a 64-key tile");
+constexpr int kTileB = kBN * kD;      // bytes of one K (or V) tile
+constexpr int kJPW = kTileB / 1024 / kNW;  // 1 KB load slices per wave per tensor per tile
+constexpr int kNLD = 2 * kJPW;        // loads per tile per wave (K and V)
+constexpr int kNBUF = 4;              // LDS ring of (K, V) tile pairs
+constexpr int kRingB = kNBUF * 2 * kTileB;
+constexpr int kStageB = 32 * kD * 2;  // per-wave output staging: 32 bf16 rows
+static_assert(kJPW == 2, "the slots below issue two loads per half tile");
 
-// s_waitcnt with vmcnt = 0 and the other counters left at their maximum.
-constexpr int kVmcnt0 = 0x0F70;
-// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle, so each
-// access of a lane is range checked against num_records (word 2) and reads 0 past it.
-constexpr int32_t kBufferWord3 = 0x00020000;
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte chunk c of key row r sits at physical chunk c ^ swz(r) (rows of 128 bytes, two
+// 16-byte chunk c of key row r sits at physical chunk c ^ swizzle(r) (rows of 128 bytes, two
 // per 256-byte bank line).
-//   K: swz = (r / 2) % 8, so the 16 consecutive rows of one ds_read_b128 pass at one logical
-//      chunk cover all 64 banks.
-//   V: swz = 2 * ((r / 2) % 2 + 2 * ((r / 8) % 2)).  One ds_read_b64_tr_b8 pass (32 lanes)
-//      reads 8 rows {B..B+3, B+8..B+11} (B a multiple of 4 with bits 1 and 3 clear) at the 4
+//   K: (r / 2) % 8, so the 16 consecutive rows of one ds_read_b128 pass at one logical chunk
+//      cover all 64 banks.
+//   V: 2 ((r / 2) % 2 + 2 ((r / 8) % 2)).  One ds_read_b64_tr_b8 pass (32 lanes) reads 8
+//      rows {B..B+3, B+8..B+11} (B a multiple of 4 with bits 1 and 3 clear) at the 4
 //      eight-byte pieces of two adjacent logical chunks; per row parity the 4 rows get 4
 //      distinct chunk pairs, so the pass covers all 64 banks.
-__device__ __forceinline__ int k_off(int r, int col) { return r * kD + (((col >> 4) ^ ((r >> 1) & 7)) << 4) + (col & 15); }
-__device__ __forceinline__ int v_off(int r, int col) {
-  const int sw = 2 * (((r >> 1) & 1) | ((r >> 2) & 2));
-  return r * kD + (((col >> 4) ^ sw) << 4) + (col & 15);
-}
-
-// Key of byte j (0..31) of a P^T / V^T operand in lane half h: the S^T accumulator element
-// j % 16 of key block j / 16, i.e. key (j/16)*32 + ((j%16)/4)*8 + 4h + j%4.
-__device__ __forceinline__ int key_of(int h, int j) { return (j >> 4) * 32 + ((j & 15) >> 2) * 8 + 4 * h + (j & 3); }
+// Both depend on r % 16 only.
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int swz_v(int r) { return 2 * (((r >> 1) & 1) | ((r >> 2) & 2)); }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   const f32x2 x = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
-__global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(Fp8Args p) {
-  extern __shared__ __align__(16) unsigned char smem[];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int l32 = lane & 31, hh = lane >> 5;
-  // the plan's launch order: blocks are dispatched round-robin over the XCDs, and each XCD's
-  // queue runs one group's query tiles side by side (they share its L2)
-  const int slot = int(blockIdx.x / kXcdCount);
-  const int unit = p.work[int(blockIdx.x % kXcdCount) * p.per_xcd + slot / kHalves];
-  const int part = slot % kHalves;  // this block's rows of the item
-  if (unit < 0) return;
-  const int head = unit / p.n_items;
-  const Item it = p.items[unit - head * p.n_items];
-  const int H = p.H;
-  const int64_t row_stride = int64_t(H) * kD;  // bytes between consecutive rows of q/k/v
+struct Fp8Params {
+  const unsigned char* __restrict__ q;
+  const unsigned char* __restrict__ k;
+  const unsigned char* __restrict__ v;
+  uint16_t* __restrict__ out;
+  const Item* __restrict__ items;
+  const int32_t* __restrict__ work;
+  int32_t* __restrict__ counters;  // kXcdCount queue counters, then the count of finished blocks
+  int persistent;                   // 0: block b runs unit work[(b % 8) * per_xcd + b / 8] only
+  float* __restrict__ part_o;
+  float* __restrict__ part_ml;
+  int H, G, frame_rows, n_items, per_xcd;
+  uint32_t tensor_bytes;  // bytes of one of q/k/v: L * H * 128
+  float scale_log2;       // log2(e) / sqrt(d) * scale_q * scale_k
+  float scale_v;
+};
+
+// Per 64-key tile a wave runs four slots of matrix ops (P^T words k = 0..7, four weights
+// each; see step_work):
+//   slot 0: S0(t) = K(t) Q0^T            | words 4..7 of block 1 (tile t-1), 2nd half of the
+//                                          loads of t+2; then block 1's slow path if due
+//   slot 1: O1 += V(t-1)^T P1^T, l1 += 1 P1^T | words 0..4 of block 0 (tile t), V(t)
+//                                          transpose reads (each d-block right after its last
+//                                          use by this slot)
+//   slot 2: S1(t) = K(t) Q1^T            | words 4..7 of block 0; then its slow path if due
+//   barrier: tile t+1 has landed for every wave
+//   slot 3: O0 += V(t)^T P0^T, l0 += 1 P0^T | words 0..4 of block 1 (tile t), K(t+1) reads,
+//                                          1st half of the loads of t+3
+// The loads of t+3 overwrite tile t-1, whose reads every wave finished before the barrier of
+// tile t.  Before the first tile, block 1's "previous tile" is empty (scores -inf, V and P
+// zero), so every iteration runs the same code; block 1's last PV runs after the loop.
+__global__ __launch_bounds__(kNW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void attn_fp8_kernel(Fp8Params p) {
+  constexpr float kLazyLog2 = 8.f;    // the running max rises only when the max grows by > 2^8
+  constexpr float kWeightLimit = 256.f;  // fast path only while every weight is <= 2^8
+  constexpr int NS = 4;               // matrix ops of an S slot: 2 k-steps x 2 key blocks
+  constexpr int NP = 5;               // of a PV slot: 4 d-blocks and the row sums
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kRingB + kNW * kStageB];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5;  // half of the wave: k sub-block of the matrix operands
+  const int l32 = lane & 31;
+  const int xcd = blockIdx.x % kXcdCount;
+  // the next unit, broadcast by wave 0 through its staging area (idle between epilogues)
+  int& s_unit = *reinterpret_cast<int*>(smem + kRingB);
+  // e4m3 1.0 in every byte: the A operand of the row-sum matrix op, kept in registers (the
+  // empty asm stops the compiler from rebuilding it before every use)
+  i32x8 ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838, 0x38383838};
+  asm volatile("" : "+a"(ones));
+
+  auto run_item = [&](const int unit) __attribute__((always_inline)) {
+  const int h = unit / p.n_items;
+  const Item it = p.items[unit - h * p.n_items];
+  const uint32_t row_bytes = uint32_t(p.H) * kD;  // bytes between consecutive rows of q/k/v
+  const int row0 = it.q_begin + wave * kWaveRows;
+  const bool wave_active = row0 < it.q_end;
   const bool causal = (it.flags & kItemCausal) != 0;
 
+  // ---- loads: lane l of slice i writes LDS chunk 64 (i kNW + wave) + l, i.e. tile row
+  // 8 wave + l / 8 + 32 i at physical chunk l % 8, which holds the row's logical chunk
+  // (l % 8) ^ swizzle(row).  The resources are based at this head's first byte and range
+  // checked against the end of the tensor (rows past it read as zero).
+  const uint32_t dma_row0 = uint32_t(8 * wave + (lane >> 3));
+  uint32_t dk[kJPW], dv[kJPW];
+#pragma unroll
+  for (int i = 0; i < kJPW; ++i) {
+    const uint32_t r = dma_row0 + uint32_t(32 * i);
+    dk[i] = r * row_bytes + uint32_t(((lane & 7) ^ swz_k(int(r))) << 4);
+    dv[i] = r * row_bytes + uint32_t(((lane & 7) ^ swz_v(int(r))) << 4);
+  }
+  auto make_rsrc = [&](const unsigned char* t) __attribute__((always_inline)) -> i32x4 {
+    const uint64_t a = reinterpret_cast<uint64_t>(t) + uint64_t(h) * kD;
+    return i32x4{__builtin_amdgcn_readfirstlane(int32_t(uint32_t(a))),
+                 __builtin_amdgcn_readfirstlane(int32_t(uint32_t(a >> 32) & 0xFFFF)),
+                 __builtin_amdgcn_readfirstlane(int32_t(p.tensor_bytes - uint32_t(h) * kD)), kBufferWord3};
+  };
+  i32x4 rsrc_k = make_rsrc(p.k), rsrc_v = make_rsrc(p.v);
+  // a buffer load may read an SGPR that a vector instruction wrote (the readfirstlane) only
+  // 5 wait states later; the loads are inline asm, unseen by the compiler's hazard checks
+  asm volatile("s_nop 4" : "+s"(rsrc_k), "+s"(rsrc_v));
+
+  // ---- LDS read offsets (bytes within a ring slot)
+  // K fragment of k-step s, key block b: key row 32 b + l32, bytes [64 s + 32 hh, +32) as two
+  // chunks (c = 0, 1); the block adds 4096 bytes (the swizzle repeats every 16 rows).
+  uint32_t koff[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) koff[s][c] = uint32_t(l32 * kD + (((4 * s + 2 * hh + c) ^ swz_k(l32)) << 4));
+  // V^T fragment of d-block db from four transpose reads m = 0..3: lane (i = lane % 16,
+  // g = lane / 16) names key row 16 m + r0 (r0 = 8 (i / 8) + 4 hh + (i / 2) % 4, which is the
+  // key of P byte 8 m + i / 2 in lane half hh) at column 32 db + 16 (g % 2) + 8 (i % 2); the
+  // instruction hands lane i byte i % 8 of the rows named by lanes 2 j + i / 8, j = 0..7.
+  // Read m adds 16 rows (2048 bytes), which keeps the swizzle.
+  uint32_t voff[4];
+  {
+    const int gi = lane & 15, gsel = (lane >> 4) & 1;
+    const int r0 = 8 * (gi >> 3) + 4 * hh + ((gi >> 1) & 3);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      voff[db] = uint32_t(kTileB + r0 * kD + (((2 * db + gsel) ^ swz_v(r0)) << 4) + 8 * (gi & 1));
+  }
+
+  // ---- tile schedule: segment 0 then segment 1, 64 keys per tile
   const int nt0 = (it.kv0_end - it.kv0_begin + kBN - 1) / kBN;
-  const int nt1 = it.kv1_end > it.kv1_begin ? (it.kv1_end - it.kv1_begin + kBN - 1) / kBN : 0;
+  const int nt1 = (it.kv1_end - it.kv1_begin + kBN - 1) / kBN;
   const int nt = nt0 + nt1;
-  auto tile_range = [&](int t, int& n0, int& nend) {
+  auto tile_range = [&](int t, int& n0, int& nend) __attribute__((always_inline)) {
     if (t < nt0) {
       n0 = it.kv0_begin + t * kBN;
       nend = it.kv0_end;
@@ -113,217 +207,396 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fp8_kernel(Fp8Args p) {
       nend = it.kv1_end;
     }
   };
-
-  // K/V tiles go straight from global memory into LDS (buffer loads with the LDS bit: no
-  // registers, no LDS write instructions).  One load moves 64 lanes x 16 bytes into 1 KB of
-  // LDS (8 rows); wave w fills slices w, w + 4, w + 8 and w + 12 of the K and of the V
-  // tile.  Lane l of slice s writes LDS chunk 64 s + l, i.e. row 8 s + l / 8 at physical
-  // chunk l % 8, which holds the row's logical chunk (l % 8) ^ swizzle(row): the swizzle is
-  // applied on the global side.  The buffer resources are based at this head's first byte and range checked
-  // against the end of the tensor (rows past it read as zero).
-  auto make_rsrc = [&](const void* t) __attribute__((always_inline)) -> i32x4 {
-    const uint64_t a = reinterpret_cast<uint64_t>(t) + uint64_t(head) * kD;
-    return i32x4{__builtin_amdgcn_readfirstlane(int32_t(uint32_t(a))),
-                 __builtin_amdgcn_readfirstlane(int32_t(uint32_t(a >> 32) & 0xFFFF)),
-                 __builtin_amdgcn_readfirstlane(int32_t(uint32_t(int64_t(p.L) * row_stride - int64_t(head) * kD))),
-                 kBufferWord3};
-  };
-  i32x4 rsrc_k = make_rsrc(p.k), rsrc_v = make_rsrc(p.v);
-  // a buffer load may read an SGPR written by a vector instruction (the readfirstlane) only
-  // 5 wait states later; the loads are inline asm, unseen by the compiler's hazard checks
-  asm volatile("s_nop 4" : "+s"(rsrc_k), "+s"(rsrc_v));
-  constexpr int kSl = kTileB / 1024 / kWaves;  // 1 KB slices of a tile per wave
-  uint32_t dk[kSl], dv[kSl];  // byte offsets of the lane's 16 bytes within a tile
-#pragma unroll
-  for (int x = 0; x < kSl; ++x) {
-    const int row = 8 * (wave + kWaves * x) + (lane >> 3);
-    dk[x] = uint32_t(row) * uint32_t(row_stride) + uint32_t(((lane & 7) ^ ((row >> 1) & 7)) << 4);
-    dv[x] = uint32_t(row) * uint32_t(row_stride) +
-            uint32_t(((lane & 7) ^ (2 * (((row >> 1) & 1) | ((row >> 2) & 2)))) << 4);
-  }
-  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) void*)smem));
-  auto dma_tile = [&](int t, int buf) __attribute__((always_inline)) {
+  // Row offset (bytes) of the first key row of tile u; tiles past the last one re-load the
+  // last tile into a slot nobody reads, so every tile issues the same number of loads.
+  auto tile_off = [&](int u) __attribute__((always_inline)) -> uint32_t {
     int n0, nend;
-    tile_range(t, n0, nend);
-    const uint32_t toff = uint32_t(n0) * uint32_t(row_stride);
+    tile_range(u < nt ? u : nt - 1, n0, nend);
+    return uint32_t(n0) * row_bytes;
+  };
+  const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
+  // load `idx` (slice idx / 2; K for even idx, V for odd) of the tile at row offset `toff`
+  // into ring slot u % kNBUF.  Issued as asm so that the compiler does not make every LDS read
+  // wait for the loads in flight; completion is ordered by the vmcnt waits before the
+  // barriers.  M0 holds the LDS destination (the nop covers the M0-write hazard).
+  auto dma_load = [&](int u, int idx, uint32_t toff) __attribute__((always_inline)) {
+    const int i = idx >> 1;
+    const uint32_t l = lds_base + uint32_t((2 * (u % kNBUF) + (idx & 1)) * kTileB + (i * kNW + wave) * 1024);
+    if (idx & 1)
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(dv[i] + toff), "s"(rsrc_v), "{m0}"(l)
+                   : "memory");
+    else
+      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(dk[i] + toff), "s"(rsrc_k), "{m0}"(l)
+                   : "memory");
+  };
+
+  const float c2 = p.scale_log2;
+  const float lazy_raw = kLazyLog2 / c2;
+  // initial running max: finite, below every finite score by more than 2^8, so the first
+  // tile (which takes the slow path) raises it; weights against it are then exactly zero
+  constexpr float kMaxInit = -0x1p100f;
+  float m_run[2], mc[2];  // running max of raw scores of this lane's query, and * c2
+  f32x16 oacc[2][4], lacc[2];
 #pragma unroll
-    for (int x = 0; x < kSl; ++x) {
-      const uint32_t lk = lds_base + uint32_t(buf * kBufB + (wave + kWaves * x) * 1024);
-      const uint32_t lv = lk + kTileB;
-      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(dk[x] + toff), "s"(rsrc_k), "{m0}"(lk)
-                   : "memory");
-      asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(dv[x] + toff), "s"(rsrc_v), "{m0}"(lv)
-                   : "memory");
+  for (int qb = 0; qb < 2; ++qb) {
+    m_run[qb] = kMaxInit;
+    mc[qb] = kMaxInit * c2;
+    lacc[qb] = f32x16{};
+#pragma unroll
+    for (int db = 0; db < 4; ++db) oacc[qb][db] = f32x16{};
+  }
+
+  i32x8 qf[2][2];  // Q fragments [qb][k-step]: lane = query row, bytes [64 s + 32 hh, +32)
+  i32x8 kf[2][2];  // K fragments of the current tile [k-step][key block]
+  i32x8 vf[4];     // V^T fragments [d-block]
+  i32x8 pb[2];     // P^T [qb]: word w = S elements 4 (w % 4) .. +3 of key block w / 4
+  float pm[2];     // max weight of the block's current tile (fast path)
+  pb[1] = i32x8{};
+#pragma unroll
+  for (int db = 0; db < 4; ++db) vf[db] = i32x8{};
+
+  auto read_k = [&](int idx) __attribute__((always_inline)) {  // half idx % 2 of fragment idx / 2
+    const int f = idx >> 1, s = f >> 1, b = f & 1, c = idx & 1;
+    const u32x4 x = *reinterpret_cast<const u32x4*>(smem + koff[s][c] + b * 32 * kD);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) kf[s][b][4 * c + j] = int(x[j]);
+  };
+  auto read_v = [&](int db, int m) __attribute__((always_inline)) {
+    const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(smem + voff[db] + m * 16 * kD));
+    vf[db][2 * m] = x[0];
+    vf[db][2 * m + 1] = x[1];
+  };
+  auto ring = [](int r) __attribute__((always_inline)) -> uint32_t { return uint32_t(r % kNBUF) * 2 * kTileB; };
+  auto other_half = [](float x) __attribute__((always_inline)) -> f32x2 {
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x), __builtin_bit_cast(uint32_t, x),
+                                                    false, false);
+    return f32x2{__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])};
+  };
+  // the four weights of word w of block qb against the running max, packed to e4m3
+  auto p_word = [&](int qb, const f32x16 (&sa)[2], int w) __attribute__((always_inline)) {
+    const int b = w >> 2, e = 4 * (w & 3);
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + j], c2, -mc[qb]));
+    const int y = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], pb[qb][w], false);
+    pb[qb][w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], y, true);
+  };
+  // Slow path of block qb's tile: mask keys past the segment end (and, for causal items,
+  // after the lane's own row), tile max, per-row raise of the running max, weights again.
+  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0) __attribute__((always_inline)) {
+    if (valid < kBN || causal) {
+      int lim = valid;
+      if (causal) lim = __builtin_elementwise_min(lim, row0 + 32 * qb + l32 - n0 + 1);
+      lim -= 4 * hh;  // key (b*32 + (i/4)*8 + 4*hh + i%4) >= limit
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          sa[b][i] = (b * 32 + (i >> 2) * 8 + (i & 3)) >= lim ? -__builtin_inff() : sa[b][i];
+    }
+    float mt = sa[0][0];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
+    const f32x2 o = other_half(mt);
+    mt = __builtin_fmaxf(o[0], o[1]);
+    // Only rows whose own max grew by more than 2^8 raise it (the branch is wave-uniform,
+    // the choice per row): a row's arithmetic never depends on the other rows' scores.
+    const bool grow = mt > m_run[qb] + lazy_raw;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? mt : m_run[qb];
+      const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * c2);
+      m_run[qb] = m_new;
+      mc[qb] = m_new * c2;
+      lacc[qb] *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) oacc[qb][db] *= alpha;
+    }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) p_word(qb, sa, w);
+  };
+
+  // Staged weights.  Word k (k = 0..7) of a block's P^T takes two steps: at step s its
+  // FMAs and exponentials, at step s + 1 its e4m3 packing and the max.  The 8 words of block
+  // 0 run over the 9 matrix-op steps of slots 1 and 2, those of block 1 over slot 3 and the
+  // next tile's slot 0, so every step carries about one word of vector work (about as long
+  // as its matrix op) and no step is without a matrix op.  fb holds the exponentials between
+  // the two stages, by word parity.  Each stage's result is pinned at its step (an empty asm
+  // that reads it): without the pins the compiler sinks pure arithmetic next to its first
+  // use, which puts dependent vector ops back to back.
+  float fb[2][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) fb[0][j] = fb[1][j] = 0.f;
+  // one step's weight work for block qb: FMAs of word `fe_k`, packing of word `pk_k`, then the
+  // exponentials of word `fe_k` (a word < 0 is none)
+  auto step_work = [&](int qb, const f32x16 (&sa)[2], int pk_k, int fe_k) __attribute__((always_inline)) {
+    if (fe_k >= 0) {
+      const int b = fe_k >> 2, e = 4 * (fe_k & 3);
+      float* f = fb[fe_k & 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[j] = __builtin_fmaf(sa[b][e + j], c2, -mc[qb]);
+      asm volatile("" ::"v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]));
+      if (fe_k == 0) pm[qb] = 0.f;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (pk_k >= 0) {
+      const float* f = fb[pk_k & 1];
+      // (both halves of the word are written: its old contents only save a move)
+      const int y = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], pb[qb][pk_k], false);
+      pb[qb][pk_k] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], y, true);
+      pm[qb] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(pm[qb], f[0]), f[1]), f[2]), f[3]);
+      asm volatile("" ::"v"(pb[qb][pk_k]), "v"(pm[qb]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (fe_k >= 0) {
+      float* f = fb[fe_k & 1];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_exp2f(f[j]);
+      asm volatile("" ::"v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]));
     }
   };
+  auto pin_p = [&](int qb) __attribute__((always_inline)) {
+    asm volatile("" ::"v"(pb[qb][0]), "v"(pb[qb][1]), "v"(pb[qb][2]), "v"(pb[qb][3]), "v"(pb[qb][4]),
+                 "v"(pb[qb][5]), "v"(pb[qb][6]), "v"(pb[qb][7]));
+  };
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool dirty) __attribute__((always_inline)) {
+    pin_p(qb);
+    asm volatile("" ::"v"(pm[qb]));
+    if (dirty || __builtin_amdgcn_ballot_w64(pm[qb] > kWeightLimit) != 0) slow_block(qb, sa, valid, n0);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // Tiles that take the slow path whatever their data, as "the next such tile after u": the
+  // first tile, the last tile of a segment that ends inside it, and for causal items every
+  // tile from the first one with a key after some row of the wave.  Block 1 checks each tile
+  // one iteration after block 0 and reuses its verdict (block 0's causal rows come first, so
+  // this is conservative for block 1).
+  const int t_rag0 = (it.kv0_end - it.kv0_begin) % kBN != 0 ? nt0 - 1 : -1;
+  const int t_rag1 = nt1 > 0 && (it.kv1_end - it.kv1_begin) % kBN != 0 ? nt - 1 : -1;
+  const int t_all = !causal ? nt : [&] {
+    const int x = row0 - (kBN - 1) - it.kv0_begin;  // tile t is masked for row0 iff t * kBN > x
+    return x < 0 ? 0 : x / kBN + 1;
+  }();
+  auto next_dirty = [&](int u) __attribute__((always_inline)) -> int {
+    int n = u + 1 > t_all ? u + 1 : t_all;
+    if (t_rag0 > u && t_rag0 < n) n = t_rag0;
+    if (t_rag1 > u && t_rag1 < n) n = t_rag1;
+    return n;
+  };
+  const f32x16 zero = {};
+  auto s_slot = [&](int qb, f32x16 (&sa)[2], bool mma, auto&& extra) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      if (mma) {
+        const int s = i >> 1, b = i & 1;
+        sa[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[s][b], qf[qb][s], s == 0 ? zero : sa[b], 0, 0, 0, 0,
+                                                                0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // the matrix op leads its step
+      extra(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto pv_slot = [&](int qb, auto&& extra) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i < 4) oacc[qb][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[i], pb[qb], oacc[qb][i], 0, 0, 0, 0,
+                                                                              0, 0);
+      else lacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb[qb], lacc[qb], 0, 0, 0, 0,
+                                                                                 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      extra(i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto barrier = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  };
 
-  dma_tile(0, 0);
-
-  // Q fragments: lane = query row, bytes [64 s + 32 hh, +32) of the row for k-step s
-  const int wrow0 = it.q_begin + part * kRows + wave * 32;  // the wave's first row
-  const int qrow = wrow0 + l32;
-  const bool q_ok = qrow < it.q_end;
-  i32x8 qf[2];
+  // prologue: tile 0 and the Q fragments land together; then tile 1 and the first half of
+  // tile 2 go in flight
   {
-    const unsigned char* qg = static_cast<const unsigned char*>(p.q) + int64_t(qrow) * row_stride + int64_t(head) * kD;
+    const uint32_t toff0 = tile_off(0);
+#pragma unroll
+    for (int idx = 0; idx < kNLD; ++idx) dma_load(0, idx, toff0);
+  }
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int qrow = row0 + 32 * qb + l32;
+    const bool ok = qrow < it.q_end;
+    const unsigned char* src = p.q + (int64_t(qrow) * p.H + h) * kD + 32 * hh;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-      if (q_ok) {
-        a = *reinterpret_cast<const u32x4*>(qg + 64 * s + 32 * hh);
-        b = *reinterpret_cast<const u32x4*>(qg + 64 * s + 32 * hh + 16);
+      if (ok) {
+        a = *reinterpret_cast<const u32x4*>(src + 64 * s);
+        b = *reinterpret_cast<const u32x4*>(src + 64 * s + 16);
       }
-      qf[s] = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(b[0]), int(b[1]), int(b[2]), int(b[3])};
+      qf[qb][s] = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(b[0]), int(b[1]), int(b[2]), int(b[3])};
     }
   }
-  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // tile 0 (and Q) have landed ...
-  __syncthreads();                       // ... for every wave
-
-  // V^T gather: transpose read m of lane (group g = lane / 16, index i = lane % 16) names
-  // key row key_of(hh, 8m + i/2) at column 16 (g & 1) + 8 (i & 1) of the d-block; the
-  // instruction hands lane i byte i % 8 of the rows named by lanes 2j + i / 8, j = 0..7.
-  const int gi = lane & 15, gsel = (lane >> 4) & 1;
-  int vrow[4];
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);
+  uint32_t toff_a = tile_off(1);  // the tile whose loads are in flight in two halves
 #pragma unroll
-  for (int m = 0; m < 4; ++m) vrow[m] = key_of(hh, 8 * m + (gi >> 1));
-  const int vcol = 16 * gsel + 8 * (gi & 1);
-
-  const float c = p.scale_log2;  // log2(e) / sqrt(d) * scale_q * scale_k
-  float m_run = -__builtin_inff(), l_run = 0.f;
-  f32x16 oacc[4];
+  for (int idx = 0; idx < kNLD; ++idx) dma_load(1, idx, toff_a);
+  toff_a = tile_off(2);
 #pragma unroll
-  for (int db = 0; db < 4; ++db) oacc[db] = f32x16{};
+  for (int idx = 0; idx < kNLD / 2; ++idx) dma_load(2, idx, toff_a);
+  barrier();
+  if (wave_active) {
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) read_k(idx);
+  }
+#pragma unroll
+  for (int s = 0; s < 2; ++s) koff[s][0] += ring(1), koff[s][1] += ring(1);  // from here on: the next tile
 
+  f32x16 s0[2], s1[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s1[b][i] = -__builtin_inff();
+  pm[1] = 0.f;
+
+  int valid_prev = kBN, n0_prev = 0;
+  int nd = 0;               // next tile that takes the slow path
+  bool dirty_prev = false;  // block 0's verdict on the previous tile (tile -1: none)
   for (int t = 0; t < nt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nt) dma_tile(t + 1, buf ^ 1);
-    const unsigned char* kb = smem + buf * kBufB;
-    const unsigned char* vb = kb + kTileB;
+    const uint32_t step_k = ring(t + 2) - ring(t + 1);  // slot advance after this tile's reads
+    const uint32_t step_v = ring(t + 1) - ring(t);
     int n0, nend;
     tile_range(t, n0, nend);
     const int valid = nend - n0;
+    const bool dirty = t == nd;
+    if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
 
-    // S^T for the four 32-key blocks of the tile
-    f32x16 sa[4];
+    if (__builtin_expect(wave_active, 1)) {
+      // slot 0 (its K fragments were read in slot 3 of the previous tile, long done)
+      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+      __builtin_amdgcn_sched_barrier(0);
+      s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
+        if (i == 0 || i == 2) dma_load(t + 2, kNLD / 2 + i / 2, toff_a);
+        step_work(1, s1, 4 + i, i < 3 ? 5 + i : -1);
+      });
+      check_block(1, s1, valid_prev, n0_prev, dirty_prev);
+      // slot 1
+      pv_slot(1, [&](int i) __attribute__((always_inline)) {
+        if (i < 4) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      sa[b] = f32x16{};
-      const int r = 32 * b + l32;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(kb + k_off(r, 64 * s + 32 * hh));
-        const u32x4 a2 = *reinterpret_cast<const u32x4*>(kb + k_off(r, 64 * s + 32 * hh + 16));
-        const i32x8 kf = {int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(a2[0]), int(a2[1]), int(a2[2]), int(a2[3])};
-        sa[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf, qf[s], sa[b], 0, 0, 0, 0, 0, 0);
-      }
-    }
-    // mask keys past the segment end (and, for causal items, after the lane's own row)
-    const bool need_mask = valid < kBN || (causal && n0 + kBN - 1 > wrow0);
-    if (need_mask) {
-      int lim = valid;
-      if (causal) lim = __builtin_elementwise_min(lim, qrow - n0 + 1);
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          if (32 * b + (i >> 2) * 8 + 4 * hh + (i & 3) >= lim) sa[b][i] = -__builtin_inff();
-    }
-    // P = 2^(S c - m) against the running max m as it stands (lazy max): the weights may
-    // reach 2^8 (exact in e4m3, whose largest value is 448) before m must rise.  A tile
-    // whose row sum exceeds 2^8 (so possibly some weight too), and the first tile, take the
-    // wave-uniform slow path: tile max, raise m, rescale, recompute P.  Byte j of the P^T
-    // operand is element j % 16 of key block j / 16.
-    i32x8 pb[2];  // keys 0..63 and 64..127 of the tile
-    float l_tile = 0.f;
-    auto weights = [&](float mneg) __attribute__((always_inline)) {
-      l_tile = 0.f;
-#pragma unroll
-      for (int w = 0; w < 16; ++w) {
-        const int b = w >> 2, e = 4 * (w & 3);
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e], c, mneg));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 1], c, mneg));
-        const float p2 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 2], c, mneg));
-        const float p3 = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + 3], c, mneg));
-        l_tile += (p0 + p1) + (p2 + p3);
-        int x = __builtin_amdgcn_cvt_pk_fp8_f32(p0, p1, 0, false);
-        x = __builtin_amdgcn_cvt_pk_fp8_f32(p2, p3, x, true);
-        pb[w >> 3][w & 7] = x;
-      }
-    };
-    bool slow = t == 0;
-    if (!slow) {
-      weights(-m_run);
-      slow = __builtin_amdgcn_ballot_w64(l_tile > 256.f) != 0;
-    }
-    if (slow) {
-      // tile max (log2 units); lanes l and l ^ 32 hold the two halves of one query's keys
-      float mt = sa[0][0];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
-      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mt), __builtin_bit_cast(uint32_t, mt),
-                                                      false, false);
-      mt = __builtin_fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
-      // Per row: the max rises only where the tile's weights could exceed 2^8 against it
-      // (and on the first tile), so a row's weights never depend on the other rows' scores.
-      const float m_new = mt * c > m_run + 8.f ? mt * c : m_run;
-      const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) oacc[db] *= alpha;
-      m_run = m_new;
-      weights(-m_run);
-    }
-    l_run += l_tile;
-    // O^T += V^T P^T per 32-row d-block
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        i32x8 vf;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const i32x2 x = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-              (__attribute__((address_space(3))) i32x2*)(vb + v_off(vrow[m] + 64 * hf, 32 * db + vcol)));
-          vf[2 * m] = x[0];
-          vf[2 * m + 1] = x[1];
+          for (int m = 0; m < 4; ++m) read_v(i, m);
         }
-        oacc[db] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf, pb[hf], oacc[db], 0, 0, 0, 0, 0, 0);
-      }
-    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // tile t + 1 has landed ...
-    __syncthreads();                       // ... for every wave
-  }
+        step_work(0, s0, i - 1, i);
+      });
+#pragma unroll
+      for (int db = 0; db < 4; ++db) voff[db] += step_v;
+      // slot 2
+      s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { step_work(0, s0, 4 + i, i < 3 ? 5 + i : -1); });
+      check_block(0, s0, valid, n0, dirty);
+    } else {
+#pragma unroll
+      for (int idx = kNLD / 2; idx < kNLD; ++idx) dma_load(t + 2, idx, toff_a);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kNLD);  // tile t+1 has landed (t+2 may be in flight) ...
+    barrier();                                   // ... for every wave
+    toff_a = tile_off(t + 3);
 
-  // ---- output: lane holds O^T[d][query] for d = 32 db + 8 (i / 4) + 4 hh + i % 4
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!q_ok) return;
-  if (it.split < 0) {
-    const float mul = p.scale_v / l_tot;
-    uint16_t* o = static_cast<uint16_t*>(p.out) + (int64_t(qrow) * H + head) * kD;
+    if (__builtin_expect(wave_active, 1)) {
+      // slot 3 (after the last tile the K reads hit a slot nobody uses)
+      pv_slot(0, [&](int i) __attribute__((always_inline)) {
+        if (i < 4) {
+          read_k(2 * i);
+          read_k(2 * i + 1);
+        }
+        if (i == 0 || i == 2) dma_load(t + 3, i / 2, toff_a);
+        step_work(1, s1, i - 1, i);
+      });
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+      for (int s = 0; s < 2; ++s) koff[s][0] += step_k, koff[s][1] += step_k;
+    } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d0 = 32 * db + 8 * r + 4 * hh;
-        const u32x2 y = {pack_bf16x2(oacc[db][4 * r] * mul, oacc[db][4 * r + 1] * mul),
-                         pack_bf16x2(oacc[db][4 * r + 2] * mul, oacc[db][4 * r + 3] * mul)};
-        *reinterpret_cast<u32x2*>(o + d0) = y;
-      }
-  } else {
-    const int64_t slot = (int64_t(it.split) * p.G + (qrow - p.frame_rows)) * H + head;
-    float* po = p.part_o + slot * kD;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int d0 = 32 * db + 8 * r + 4 * hh;
-        *reinterpret_cast<float4*>(po + d0) =
-            make_float4(oacc[db][4 * r] * p.scale_v, oacc[db][4 * r + 1] * p.scale_v,
-                        oacc[db][4 * r + 2] * p.scale_v, oacc[db][4 * r + 3] * p.scale_v);
-      }
-    if (hh == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run, l_tot);
+      for (int idx = 0; idx < kNLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
+    }
+    valid_prev = valid;
+    n0_prev = n0;
+    dirty_prev = dirty;
   }
+  __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no load may still write this block's LDS at exit
+  if (wave_active) {  // block 1 of the last tile
+    s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { step_work(1, s1, 4 + i, i < 3 ? 5 + i : -1); });
+    check_block(1, s1, valid_prev, n0_prev, dirty_prev);
+    pv_slot(1, [&](int) __attribute__((always_inline)) {});
+  }
+  if (!wave_active) return;
+
+  // ---- Output.  A lane holds 4-column pieces of its row spread over the row; each 32-row
+  // block goes through this wave's LDS staging area (16-byte chunks XOR-swizzled by row) and
+  // leaves as whole rows, 16 lanes x 16 bytes per row.  Global-leg partials (fp32, already
+  // times scale_v) go straight out.
+  unsigned char* const stage = smem + kRingB + wave * kStageB;
+  // lane indices redefined here (empty asm) so that the staging addresses are computed here
+  // and not hoisted out of the unit loop into the tile loop's register budget
+  int orow_l = l32, olane = lane;
+  asm volatile("" : "+v"(orow_l), "+v"(olane));
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int rows_here = it.q_end - (row0 + 32 * qb);
+    if (rows_here <= 0) continue;
+    const float l_tot = lacc[qb][0];  // every element holds the row sum over both halves
+    if (it.split < 0) {
+      const float mul = p.scale_v / l_tot;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int off = (32 * db + 8 * g4) * 2 + 8 * hh;  // byte offset in the row
+          unsigned char* dst = stage + orow_l * (kD * 2) + (((off >> 4) ^ (orow_l & 15)) << 4) + (off & 15);
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{pack_bf16x2(oacc[qb][db][4 * g4] * mul, oacc[qb][db][4 * g4 + 1] * mul),
+                    pack_bf16x2(oacc[qb][db][4 * g4 + 2] * mul, oacc[qb][db][4 * g4 + 3] * mul)};
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = k * 64 + olane, r = j >> 4, c = j & 15;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (kD * 2) + ((c ^ (r & 15)) << 4));
+        if (r < rows_here)
+          *reinterpret_cast<u32x4*>(p.out + (int64_t(row0 + 32 * qb + r) * p.H + h) * kD + c * 8) = x;
+      }
+    } else {
+      const int qrow = row0 + 32 * qb + l32;
+      if (qrow < it.q_end) {
+        const int64_t slot = (int64_t(it.split) * p.G + (qrow - p.frame_rows)) * p.H + h;
+        float* po = p.part_o + slot * kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g4 + 4 * hh) =
+                f32x4{oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
+                      oacc[qb][db][4 * g4 + 3]} * p.scale_v;
+        if (hh == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run[qb] * c2, l_tot);
+      }
+    }
+  }
+  };  // run_item
+
+  for (int n = 0;; ++n) {
+    // The barrier also orders this block's LDS use: every wave has finished the previous unit
+    // before the next unit's prologue refills the ring.  Without queues (few units) block b
+    // runs the one unit at its place in the launch order.
+    if (wave == 0) {
+      const int u = p.persistent ? fetch_unit(p.work, p.counters, p.per_xcd, xcd, lane)
+                                 : (n == 0 ? p.work[xcd * p.per_xcd + int(blockIdx.x) / kXcdCount] : -1);
+      if (lane == 0) s_unit = u;
+    }
+    __syncthreads();
+    const int unit = __builtin_amdgcn_readfirstlane(s_unit);
+    if (unit < 0) break;
+    run_item(unit);
+  }
+  if (p.persistent && tid == 0) finish_persistent(p.counters);  // the last block resets the queues
 }
 
 // Merge of the global leg's key splits (as for the bf16 path): for each (global row, head),
@@ -357,25 +630,39 @@ __global__ __launch_bounds__(kCombineThreads) void combine_fp8_kernel(const floa
   }
   const float inv = 1.f / den;
   const int64_t orow = (int64_t(frame_rows) * H + slot) * kD + c4;  // row frame_rows + slot / H, head slot % H
-  const __bf16 b0 = (__bf16)(num.x * inv), b1 = (__bf16)(num.y * inv), b2 = (__bf16)(num.z * inv),
-               b3 = (__bf16)(num.w * inv);
-  const uint32_t lo = uint32_t(__builtin_bit_cast(uint16_t, b0)) | (uint32_t(__builtin_bit_cast(uint16_t, b1)) << 16);
-  const uint32_t hi = uint32_t(__builtin_bit_cast(uint16_t, b2)) | (uint32_t(__builtin_bit_cast(uint16_t, b3)) << 16);
-  *reinterpret_cast<uint2*>(out + orow) = make_uint2(lo, hi);
+  *reinterpret_cast<uint2*>(out + orow) =
+      make_uint2(pack_bf16x2(num.x * inv, num.y * inv), pack_bf16x2(num.z * inv, num.w * inv));
 }
 
 }  // namespace
 
-hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream) {
-  if (a.d != kD) return hipErrorInvalidValue;
-  const int grid = kXcdCount * a.per_xcd * kHalves;
-  if (grid < 1) return hipSuccess;
-  hipLaunchKernelGGL(attn_fp8_kernel, dim3(grid), dim3(kThreads), 2 * kBufB, stream, a);
+hipError_t launch_forward_fp8(const ForwardArgs& a, float scale_v, hipStream_t stream) {
+  if (a.d != kD || a.block_m != kNW * kWaveRows || a.out_f32 || a.tile_list) return hipErrorInvalidValue;
+  Fp8Params p;
+  p.q = static_cast<const unsigned char*>(a.q);
+  p.k = static_cast<const unsigned char*>(a.k);
+  p.v = static_cast<const unsigned char*>(a.v);
+  p.out = static_cast<uint16_t*>(a.out);
+  p.items = a.items;
+  p.work = a.work;
+  p.counters = a.counters;
+  p.persistent = a.persistent;
+  p.part_o = a.part_o;
+  p.part_ml = a.part_ml;
+  p.H = a.H;
+  p.G = a.G;
+  p.frame_rows = a.frame_rows;
+  p.n_items = a.n_items;
+  p.per_xcd = a.work_per_xcd;
+  p.tensor_bytes = uint32_t(a.L) * uint32_t(a.H) * uint32_t(kD);
+  p.scale_log2 = a.scale_log2;
+  p.scale_v = scale_v;
+  if (a.grid < 1) return hipSuccess;
+  hipLaunchKernelGGL(attn_fp8_kernel, dim3(a.grid), dim3(kNW * 64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_splits <= 1) return e;
   hipLaunchKernelGGL(combine_fp8_kernel, dim3((a.G * a.H + kCombineSlots - 1) / kCombineSlots), dim3(kCombineThreads),
-                     0, stream, a.part_o, a.part_ml, static_cast<uint16_t*>(a.out), a.G, a.H, a.n_splits,
-                     a.frame_rows);
+                     0, stream, a.part_o, a.part_ml, p.out, a.G, a.H, a.n_splits, a.frame_rows);
   return hipGetLastError();
 }
 

@@ -51,6 +51,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "attn_common.h"
 #include "launch.h"
 
 namespace wa {
@@ -87,10 +88,6 @@ __device__ __forceinline__ int swz(int row) {
   if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   else return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
-
-// s_waitcnt with vmcnt = 0 (lgkmcnt = 0) and the other counters left at their maximum.
-constexpr int kVmcnt0 = 0x0F70;
-constexpr int kLgkmcnt0 = 0xC07F;
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -129,44 +126,6 @@ struct AttnParamsTL : AttnParams {
   const int32_t* __restrict__ tiles;
   int T, S, K, radius, n_chunks;
 };
-
-// Next work unit for a block on XCD `xcd`, run by one whole wave: its own XCD's queue first
-// (the queue rows of the launch order: window units, then global-leg units, then -1
-// padding), then the other XCDs' queues (work stealing at the end of the launch).  -1 when
-// every queue is empty.  A queue counter that has passed the queue's last unit marks it
-// empty; lanes 0..7 probe all eight queues at once, so a block that runs out costs two
-// round trips to memory, not eight.
-__device__ __forceinline__ int fetch_unit(const int32_t* __restrict__ work, int32_t* __restrict__ counters,
-                                          int per_xcd, int xcd, int lane) {
-  int u = -1;
-  if (lane == 0) {
-    const int i = atomicAdd(counters + xcd, 1);
-    if (i < per_xcd) u = work[xcd * per_xcd + i];
-  }
-  u = __builtin_amdgcn_readfirstlane(u);
-  while (u < 0) {
-    const int y = lane & (kXcdCount - 1);
-    const int x = xcd + y < kXcdCount ? xcd + y : xcd + y - kXcdCount;
-    bool open = false;
-    if (lane < kXcdCount) {
-      const int c = __hip_atomic_load(counters + x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      open = c < per_xcd && work[x * per_xcd + c] >= 0;
-    }
-    const uint64_t m = __builtin_amdgcn_ballot_w64(open);
-    if (m == 0) break;  // every queue is empty
-    const int x0 = (xcd + __builtin_ctzll(m)) % kXcdCount;
-    if (lane == 0) {
-      const int i = atomicAdd(counters + x0, 1);
-      if (i < per_xcd) u = work[x0 * per_xcd + i];
-    }
-    u = __builtin_amdgcn_readfirstlane(u);
-  }
-  return u;
-}
-
-// Word 3 of a raw buffer resource on gfx9 parts: 32-bit data format, no swizzle, so each
-// access of a lane is range checked against num_records (word 2) and reads 0 past it.
-constexpr int32_t kBufferWord3 = 0x00020000;
 
 // One block = 4 waves (one per SIMD); one wave = 64 query rows as two 32-row blocks
 // (qb = 0, 1).  Every K and V fragment read from LDS feeds both blocks' matrix ops.
@@ -869,14 +828,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
     if (unit < 0) break;
     run_item(unit);
   }
-  // The last block to finish resets the queue counters for the next launch (every block has
-  // made its last fetch when it counts itself finished).
-  if (p.persistent && tid == 0) {
-    __threadfence();
-    if (atomicAdd(p.counters + kXcds, 1) == int(gridDim.x) - 1) {
-      for (int x = 0; x <= kXcds; ++x) atomicExch(p.counters + x, 0);
-    }
-  }
+  if (p.persistent && tid == 0) finish_persistent(p.counters);  // the last block resets the queues
 }
 
 // Merge the global leg's key splits: for each (global row, head), with m_s in log2 units,

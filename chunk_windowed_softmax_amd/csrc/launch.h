@@ -67,23 +67,10 @@ struct PrologueArgs {
 // Enqueue the QK-RMSNorm + rotary-embedding pass (q and k in one launch).
 hipError_t launch_qk_norm_rope(const PrologueArgs& a, hipStream_t stream);
 
-struct Fp8Args {
-  const void* q;          // e4m3 codes [L, H, d]
-  const void* k;
-  const void* v;
-  void* out;              // bf16 [L, H, d]
-  const Item* items;      // device copy of the plan's items
-  const int32_t* work;    // device copy of the launch order (kXcdCount * per_xcd units, -1 = none)
-  int per_xcd;
-  int n_items, H, G, L, d, frame_rows, n_splits;
-  float* part_o;          // [n_splits, G, H, d] fp32 (global-leg partials)
-  float* part_ml;         // [n_splits, G, H, 2] fp32
-  float scale_log2;       // log2(e) / sqrt(d) * scale_q * scale_k
-  float scale_v;
-};
-
-// Enqueue the FP8 attention pass (one block per item and head) and, when the global leg is
-// split, its merge.  d must be 128.
-hipError_t launch_forward_fp8(const Fp8Args& a, hipStream_t stream);
+// Enqueue the FP8 attention pass and, when the global leg is split, its merge.  `a` is set
+// up as for launch_forward (bf16 output, no tile lists, d = 128) with q, k, v pointing at
+// e4m3 codes and scale_log2 = log2(e) / sqrt(d) * scale_q * scale_k; the output is
+// multiplied by scale_v.
+hipError_t launch_forward_fp8(const ForwardArgs& a, float scale_v, hipStream_t stream);
 
 }  // namespace wa

@@ -152,3 +152,20 @@ def test_fp8_covers_every_row_and_is_deterministic(gpu_lib):
     torch.cuda.synchronize()
     assert not torch.isnan(out).any()
     assert torch.equal(out, again)
+
+
+def test_fp8_constant_values_exact(gpu_lib):
+    """Every value row the same vector: whatever the weights, the output is that vector,
+    provided each row is normalised by the sum of exactly the (e4m3-rounded) weights that
+    multiply V.  Normalising by the unrounded sum would leave the rounding's relative error
+    (up to 2^-4 per weight) in the output.  Random q and k at a wide score range, so many
+    weights are far from representable, and the persistent launch of the ragged workload."""
+    w = WORKLOADS["ragged"]
+    g = torch.Generator().manual_seed(7)
+    q8, sq = quantize_e4m3(torch.randn(w.L, w.H, w.d, generator=g) * 3.0)
+    k8, sk = quantize_e4m3(torch.randn(w.L, w.H, w.d, generator=g) * 3.0)
+    row, sv = quantize_e4m3(torch.randn(1, 1, w.d, generator=g))
+    v8 = row.expand(w.L, w.H, w.d).contiguous()
+    got = _run(gpu_lib, _plan(gpu_lib, w), q8, k8, v8, sq, sk, sv)
+    want = np.broadcast_to(decode_e4m3(row) * sv, got.shape)
+    _check_exact(got, want, "constant values")
