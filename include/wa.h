@@ -272,13 +272,15 @@ int wa_plan_launch_order(const wa_plan* plan, int32_t* dst, size_t n);
  * overlapping no input.
  * Computes out = softmax(scale_q scale_k q k^T / sqrt(d)) (scale_v v) over each row's kept
  * keys, like wa_forward: scores and the softmax in fp32, the softmax weights rounded to e4m3
- * for the second product (the one approximation beyond the inputs), the row sums over the
- * fp32 weights, output rounded to bf16.
+ * for the second product (the one approximation beyond the inputs), each row divided by the
+ * sum of exactly those rounded weights (so the weights applied to v sum to one), output
+ * rounded to bf16.
  * stream: a hipStream_t (NULL = default).  Enqueues the kernels and returns without
  * synchronising; shares the plan's workspace with wa_forward and is ordered with the
  * plan's other calls in the same way (see wa_forward).
  * Errors: WA_ERR_INVALID (NULL plan or tensor, misalignment, overlap, bad scale),
- * WA_ERR_UNSUPPORTED (d != 128), WA_ERR_ALLOC, WA_ERR_HIP.
+ * WA_ERR_UNSUPPORTED (d != 128, or a plan of wa_blocksparse_plan_create), WA_ERR_ALLOC,
+ * WA_ERR_HIP.
  */
 int wa_forward_fp8(const wa_plan* plan, const void* q, const void* k, const void* v, float scale_q,
                    float scale_k, float scale_v, void* out, void* stream);
