@@ -155,6 +155,11 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   static_assert(NJ % kNW == 0, "tile slices must divide evenly over the waves");
   constexpr float kLazyLog2 = 8.f;              // slow path: rescale only when the max grows by > 2^8
   constexpr float kRowSumLimit = 256.f;         // fast path only while every P of the tile <= 2^8
+  // d = 64: the row sums of P come from matrix ops against an all-ones operand (four per
+  // block and tile, at the end of the PV slot) instead of vector adds.  At d = 64 a tile has
+  // half the matrix work of d = 128 and the same vector work, so the vector ALU is the
+  // bound and the trade pays; at d = 128 the matrix pipe is the busier one and it would not.
+  constexpr bool ONES = D == 64;
 
   constexpr int NBUF = 4;                       // LDS ring of (K, V) tile pairs
   constexpr int RINGB = NBUF * 2 * TILEB;       // bytes of the ring
@@ -171,6 +176,10 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   // Persistent blocks, one per CU: each runs work units (fetch_unit) until all queues are
   // empty.  Blocks are dispatched round-robin over the XCDs.
   const int xcd = blockIdx.x % kXcds;
+  // ONES: bf16 1.0 in every element, the A operand of the row-sum matrix ops, kept in AGPRs
+  // (the empty asm stops the compiler from rebuilding it before every use)
+  bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+  if constexpr (ONES) asm volatile("" : "+a"(ones));
   // The next unit, broadcast by wave 0; it shares wave 0's staging area, which is idle from
   // the end of one unit's epilogue to the next unit's epilogue.
   int& s_unit = *reinterpret_cast<int*>(smem + RINGB);
@@ -297,11 +306,17 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
 
   float m_run[2], mc[2], l_run[2];  // running max of raw scores (this lane's queries), * c2, sum
   f32x16 oacc[2][DB];
+  f32x16 lacc[2];  // ONES: row sums (every element of a lane holds its query's sum)
+  float pm[2];     // ONES: max weight of the block's current tile
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     m_run[qb] = kMaxInit;
     mc[qb] = kMaxInit * c2;
     l_run[qb] = 0.f;
+    if constexpr (ONES) {
+      lacc[qb] = f32x16{};
+      pm[qb] = 0.f;
+    }
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -363,7 +378,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
     const int b = n >> 3, e = 2 * (n & 7);
     const float x0 = sa[b][e], x1 = sa[b][e + 1];
     pw[qb][n] = cvt_bf16x2(fast_exp2(__builtin_fmaf(x0, c2, -mcq)), fast_exp2(__builtin_fmaf(x1, c2, -mcq)));
-    add_pair(qb, pw[qb][n]);
+    if constexpr (!ONES) add_pair(qb, pw[qb][n]);
   };
   // Value of the lane 32 apart (the other half of the same query's keys), in both orders.
   auto other_half = [](float x) __attribute__((always_inline)) -> f32x2 {
@@ -404,10 +419,12 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   // running max when it grew by more than 2^8, when
   //   - it is the unit's first tile or has masked keys (segment end, causal diagonal): known
   //     before the tile, one scalar compare per tile;
-  //   - some row sum of the tile exceeds 2^8 (any P above 2^8 makes it so).
+  //   - some row sum of the tile exceeds 2^8 (any P above 2^8 makes it so; ONES: some P
+  //     exceeds 2^8, from one max per pair).
   constexpr int NS = 2 * KS;                // matrix ops of an S slot
-  constexpr int NP = 4 * DB;                // matrix ops of a PV slot
-  static_assert(NS % 4 == 0 && NP % 4 == 0 && (2 * KS) % NP == 0 && 16 % NP == 0 && NLD % 2 == 0,
+  constexpr int NPV = 4 * DB;               // PV matrix ops of a PV slot
+  constexpr int NP = NPV + (ONES ? 4 : 0);  // all matrix ops of a PV slot (ONES: + the row sums)
+  static_assert(NS % 4 == 0 && NPV % 4 == 0 && (2 * KS) % NPV == 0 && 16 % NPV == 0 && NLD % 2 == 0,
                 "slot work must divide evenly over the steps");
   auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool masked) __attribute__((always_inline)) {
     if constexpr (TL) {
@@ -463,7 +480,8 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
       const float alpha = fast_exp2((m_run[qb] - m_new) * c2);
       m_run[qb] = m_new;
       mc[qb] = m_new * c2;
-      l_run[qb] *= alpha;
+      if constexpr (ONES) lacc[qb] *= alpha;
+      else l_run[qb] *= alpha;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -495,17 +513,24 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
       const int fs = k * N / 8;
       const int n = lo + k, b = n >> 3, e = 2 * (n & 7);
       const int f_pack = pv ? fs + 2 : fs + 3, f_sum = f_pack + 1;
-      if (f_sum == i) {
-        if (pv) {
-          dot_pair(qb, k, pw[qb][n]);
-        } else {
-          add_pair(qb, pw[qb][n]);
-          asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
+      if constexpr (!ONES) {
+        if (f_sum == i) {
+          if (pv) {
+            dot_pair(qb, k, pw[qb][n]);
+          } else {
+            add_pair(qb, pw[qb][n]);
+            asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
+          }
         }
       }
       if (f_pack == i) {
         pw[qb][n] = cvt_bf16x2(fa[k], fb[k]);
-        asm volatile("" ::"v"(pw[qb][n]));
+        if constexpr (ONES) {
+          pm[qb] = __builtin_fmaxf(__builtin_fmaxf(pm[qb], fa[k]), fb[k]);
+          asm volatile("" ::"v"(pw[qb][n]), "v"(pm[qb]));
+        } else {
+          asm volatile("" ::"v"(pw[qb][n]));
+        }
       }
       if (fs + 1 == i) {
         fa[k] = fast_exp2(fa[k]);
@@ -513,6 +538,9 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
         asm volatile("" ::"v"(fa[k]), "v"(fb[k]));
       }
       if (fs == i) {
+        if constexpr (ONES) {
+          if (pv && k == 0) pm[qb] = 0.f;  // the block's first pair of the tile
+        }
         const float x0 = sa[b][e], x1 = sa[b][e + 1];
         fa[k] = __builtin_fmaf(x0, c2, -mc[qb]);
         fb[k] = __builtin_fmaf(x1, c2, -mc[qb]);
@@ -530,10 +558,15 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool dirty, bool masked)
                          __attribute__((always_inline)) {
     pin_p(qb);
-    asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
-    if (dirty || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
-      slow_block(qb, sa, valid, n0, masked);
-    l_run[qb] += rs[qb][0] + rs[qb][1];
+    if constexpr (ONES) {
+      asm volatile("" ::"v"(pm[qb]));
+      if (dirty || __builtin_amdgcn_ballot_w64(pm[qb] > kRowSumLimit) != 0) slow_block(qb, sa, valid, n0, masked);
+    } else {
+      asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
+      if (dirty || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
+        slow_block(qb, sa, valid, n0, masked);
+      l_run[qb] += rs[qb][0] + rs[qb][1];
+    }
     __builtin_amdgcn_sched_barrier(0);
   };
   // Tiles that take the slow path whatever their data (see above), as "the next such tile
@@ -556,14 +589,18 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   // PV slot of block qb: N matrix ops (when `mma`), then the tail steps for the staged pairs.
   // Steps after the last matrix op of a slot in which the staged pairs finish: the last pair
   // starts at step 7 * N / 8 and ends at most 4 steps later (N = NS = NP).
-  static_assert(NS == NP, "S and PV slots have the same number of steps");
+  static_assert(NS == NPV, "S and PV slots have the same number of value steps");
   constexpr int kTail = 7 * NS / 8 + 5 - NS;
+  constexpr int kTailP = 7 * NP / 8 + 5 - NP;
   auto pv_slot = [&](int qb, bool mma, auto&& extra) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NP + kTail; ++i) {
-      if (mma && i < NP) {
+    for (int i = 0; i < NP + kTailP; ++i) {
+      if (mma && i < NPV) {
         const int b = i / (2 * DB), tt = (i / DB) & 1, db = i % DB;
         oacc[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(b, tt, db), pfrag(qb, b, tt), oacc[qb][db], 0, 0, 0);
+      } else if (ONES && mma && i < NP) {
+        const int j = i - NPV;  // 16-key piece j of the tile: l += 1 P^T
+        lacc[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ones, pfrag(qb, j >> 1, j & 1), lacc[qb], 0, 0, 0);
       }
       extra(i);
       __builtin_amdgcn_sched_barrier(0);
@@ -665,7 +702,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
       // slot 1
       rs[0][0] = rs[0][1] = 0.f;
       pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
-        if (i < NP) {
+        if (i < NPV) {
           read_v(2 * i);
           read_v(2 * i + 1);
         }
@@ -704,10 +741,10 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
       // slot 3 (after the last tile the K reads hit a buffer nobody uses)
       rs[1][0] = rs[1][1] = 0.f;
       pv_slot(0, true, [&](int i) __attribute__((always_inline)) {
-        if (i < NP) {
+        if (i < NPV) {
 #pragma unroll
-          for (int r = 0; r < 2 * KS / NP; ++r) read_k(i * (2 * KS / NP) + r);
-          if (i % (NP / (NLD / 2)) == 0) dma_load(t + 3, i / (NP / (NLD / 2)), toff_a);
+          for (int r = 0; r < 2 * KS / NPV; ++r) read_k(i * (2 * KS / NPV) + r);
+          if (i % (NPV / (NLD / 2)) == 0) dma_load(t + 3, i / (NPV / (NLD / 2)), toff_a);
         }
         stage_at(1, s1, 0, NP, i);
       });
@@ -745,7 +782,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   constexpr int EB = OUT_F32 ? 4 : 2;  // bytes per element of the final output
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = [&] {
+    const float l_tot = ONES ? lacc[qb][0] : [&] {
       const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, l_run[qb]),
                                                       __builtin_bit_cast(uint32_t, l_run[qb]), false, false);
       return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
