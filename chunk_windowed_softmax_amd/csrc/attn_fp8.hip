@@ -283,7 +283,10 @@ void attn_fp8_kernel(Fp8Params p) {
   };
   // Slow path of block qb's tile: mask keys past the segment end (and, for causal items,
   // after the lane's own row), tile max, per-row raise of the running max, weights again.
-  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0) __attribute__((always_inline)) {
+  auto slow_block = [&](int qb, f32x16 (&sa)[2], int t) __attribute__((always_inline)) {
+    int n0, nend;
+    tile_range(t, n0, nend);
+    const int valid = nend - n0;
     if (valid < kBN || causal) {
       int lim = valid;
       if (causal) lim = __builtin_elementwise_min(lim, row0 + 32 * qb + l32 - n0 + 1);
@@ -360,10 +363,11 @@ void attn_fp8_kernel(Fp8Params p) {
     asm volatile("" ::"v"(pb[qb][0]), "v"(pb[qb][1]), "v"(pb[qb][2]), "v"(pb[qb][3]), "v"(pb[qb][4]),
                  "v"(pb[qb][5]), "v"(pb[qb][6]), "v"(pb[qb][7]));
   };
-  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool dirty) __attribute__((always_inline)) {
+  // block qb's verdict on tile t (its scores in sa)
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int t, bool dirty) __attribute__((always_inline)) {
     pin_p(qb);
     asm volatile("" ::"v"(pm[qb]));
-    if (dirty || __builtin_amdgcn_ballot_w64(pm[qb] > kWeightLimit) != 0) slow_block(qb, sa, valid, n0);
+    if (dirty || __builtin_amdgcn_ballot_w64(pm[qb] > kWeightLimit) != 0) slow_block(qb, sa, t);
     __builtin_amdgcn_sched_barrier(0);
   };
   // Tiles that take the slow path whatever their data, as "the next such tile after u": the
@@ -461,75 +465,70 @@ void attn_fp8_kernel(Fp8Params p) {
     for (int i = 0; i < 16; ++i) s1[b][i] = -__builtin_inff();
   pm[1] = 0.f;
 
-  int valid_prev = kBN, n0_prev = 0;
+  if (!wave_active) {
+    // a wave without rows in this item takes only its share of the loads and the barriers
+    for (int t = 0; t < nt; ++t) {
+#pragma unroll
+      for (int idx = kNLD / 2; idx < kNLD; ++idx) dma_load(t + 2, idx, toff_a);
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kNLD);
+      barrier();
+      toff_a = tile_off(t + 3);
+#pragma unroll
+      for (int idx = 0; idx < kNLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no load may still write this block's LDS at exit
+    return;
+  }
   int nd = 0;               // next tile that takes the slow path
   bool dirty_prev = false;  // block 0's verdict on the previous tile (tile -1: none)
   for (int t = 0; t < nt; ++t) {
     const uint32_t step_k = ring(t + 2) - ring(t + 1);  // slot advance after this tile's reads
     const uint32_t step_v = ring(t + 1) - ring(t);
-    int n0, nend;
-    tile_range(t, n0, nend);
-    const int valid = nend - n0;
     const bool dirty = t == nd;
     if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
 
-    if (__builtin_expect(wave_active, 1)) {
-      // slot 0 (its K fragments were read in slot 3 of the previous tile, long done)
-      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
-      __builtin_amdgcn_sched_barrier(0);
-      s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
-        if (i == 0 || i == 2) dma_load(t + 2, kNLD / 2 + i / 2, toff_a);
-        step_work(1, s1, 4 + i, i < 3 ? 5 + i : -1);
-      });
-      check_block(1, s1, valid_prev, n0_prev, dirty_prev);
-      // slot 1
-      pv_slot(1, [&](int i) __attribute__((always_inline)) {
-        if (i < 4) {
+    // slot 0 (its K fragments were read in slot 3 of the previous tile, long done)
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
+      if (i == 0 || i == 2) dma_load(t + 2, kNLD / 2 + i / 2, toff_a);
+      step_work(1, s1, 4 + i, i < 3 ? 5 + i : -1);
+    });
+    check_block(1, s1, t - 1, dirty_prev);
+    // slot 1
+    pv_slot(1, [&](int i) __attribute__((always_inline)) {
+      if (i < 4) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) read_v(i, m);
-        }
-        step_work(0, s0, i - 1, i);
-      });
+        for (int m = 0; m < 4; ++m) read_v(i, m);
+      }
+      step_work(0, s0, i - 1, i);
+    });
 #pragma unroll
-      for (int db = 0; db < 4; ++db) voff[db] += step_v;
-      // slot 2
-      s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { step_work(0, s0, 4 + i, i < 3 ? 5 + i : -1); });
-      check_block(0, s0, valid, n0, dirty);
-    } else {
-#pragma unroll
-      for (int idx = kNLD / 2; idx < kNLD; ++idx) dma_load(t + 2, idx, toff_a);
-    }
+    for (int db = 0; db < 4; ++db) voff[db] += step_v;
+    // slot 2
+    s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { step_work(0, s0, 4 + i, i < 3 ? 5 + i : -1); });
+    check_block(0, s0, t, dirty);
     __builtin_amdgcn_s_waitcnt(0x0F70 | kNLD);  // tile t+1 has landed (t+2 may be in flight) ...
     barrier();                                   // ... for every wave
     toff_a = tile_off(t + 3);
-
-    if (__builtin_expect(wave_active, 1)) {
-      // slot 3 (after the last tile the K reads hit a slot nobody uses)
-      pv_slot(0, [&](int i) __attribute__((always_inline)) {
-        if (i < 4) {
-          read_k(2 * i);
-          read_k(2 * i + 1);
-        }
-        if (i == 0 || i == 2) dma_load(t + 3, i / 2, toff_a);
-        step_work(1, s1, i - 1, i);
-      });
+    // slot 3 (after the last tile the K reads hit a slot nobody uses)
+    pv_slot(0, [&](int i) __attribute__((always_inline)) {
+      if (i < 4) {
+        read_k(2 * i);
+        read_k(2 * i + 1);
+      }
+      if (i == 0 || i == 2) dma_load(t + 3, i / 2, toff_a);
+      step_work(1, s1, i - 1, i);
+    });
 #pragma unroll
-      for (int s = 0; s < 2; ++s) koff[s][0] += step_k, koff[s][1] += step_k;
-    } else {
-#pragma unroll
-      for (int idx = 0; idx < kNLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
-    }
-    valid_prev = valid;
-    n0_prev = n0;
+    for (int s = 0; s < 2; ++s) koff[s][0] += step_k, koff[s][1] += step_k;
     dirty_prev = dirty;
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no load may still write this block's LDS at exit
-  if (wave_active) {  // block 1 of the last tile
-    s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { step_work(1, s1, 4 + i, i < 3 ? 5 + i : -1); });
-    check_block(1, s1, valid_prev, n0_prev, dirty_prev);
-    pv_slot(1, [&](int) __attribute__((always_inline)) {});
-  }
-  if (!wave_active) return;
+  // block 1 of the last tile
+  s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { step_work(1, s1, 4 + i, i < 3 ? 5 + i : -1); });
+  check_block(1, s1, nt - 1, dirty_prev);
+  pv_slot(1, [&](int) __attribute__((always_inline)) {});
 
   // ---- Output.  A lane holds 4-column pieces of its row spread over the row; each 32-row
   // block goes through this wave's LDS staging area (16-byte chunks XOR-swizzled by row) and

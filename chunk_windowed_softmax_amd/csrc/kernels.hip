@@ -426,7 +426,8 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   constexpr int NP = NPV + (ONES ? 4 : 0);  // all matrix ops of a PV slot (ONES: + the row sums)
   static_assert(NS % 4 == 0 && NPV % 4 == 0 && (2 * KS) % NPV == 0 && 16 % NPV == 0 && NLD % 2 == 0,
                 "slot work must divide evenly over the steps");
-  auto slow_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool masked) __attribute__((always_inline)) {
+  // Slow path of block qb on tile t (TL: first key row n0 and whether the tile is masked).
+  auto slow_block = [&](int qb, f32x16 (&sa)[2], int t, int n0, bool masked) __attribute__((always_inline)) {
     if constexpr (TL) {
       if (masked) {
         // the window rule for this lane's query row: frame rows keep their window's chunk
@@ -453,17 +454,22 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
             sa[b][i] = keep ? sa[b][i] : -__builtin_inff();
           }
       }
-    } else if (valid < kBN || causal) {
-      // tile keys at or past `lim` are masked: the segment end, and for causal items also
-      // every key after this lane's own query row
-      int lim = valid;
-      if (causal) lim = __builtin_elementwise_min(lim, row0 + 32 * qb + l32 - n0 + 1);
-      lim -= 4 * hh;  // key (b*32 + (i/4)*8 + 4*hh + i%4) >= valid
+    } else {
+      int k0, kend;
+      tile_range(t, k0, kend);
+      const int valid = kend - k0;
+      if (valid < kBN || causal) {
+        // tile keys at or past `lim` are masked: the segment end, and for causal items also
+        // every key after this lane's own query row
+        int lim = valid;
+        if (causal) lim = __builtin_elementwise_min(lim, row0 + 32 * qb + l32 - k0 + 1);
+        lim -= 4 * hh;  // key (b*32 + (i/4)*8 + 4*hh + i%4) >= valid
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
+        for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          sa[b][i] = (b * 32 + (i >> 2) * 8 + (i & 3)) >= lim ? -__builtin_inff() : sa[b][i];
+          for (int i = 0; i < 16; ++i)
+            sa[b][i] = (b * 32 + (i >> 2) * 8 + (i & 3)) >= lim ? -__builtin_inff() : sa[b][i];
+      }
     }
     float mt = sa[0][0];
 #pragma unroll
@@ -555,16 +561,17 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
                  "v"(pw[qb][5]), "v"(pw[qb][6]), "v"(pw[qb][7]), "v"(pw[qb][8]), "v"(pw[qb][9]), "v"(pw[qb][10]),
                  "v"(pw[qb][11]), "v"(pw[qb][12]), "v"(pw[qb][13]), "v"(pw[qb][14]), "v"(pw[qb][15]));
   };
-  auto check_block = [&](int qb, f32x16 (&sa)[2], int valid, int n0, bool dirty, bool masked)
+  // block qb's verdict on tile t (its scores in sa; TL: n0, masked from the tile's entry)
+  auto check_block = [&](int qb, f32x16 (&sa)[2], int t, int n0, bool dirty, bool masked)
                          __attribute__((always_inline)) {
     pin_p(qb);
     if constexpr (ONES) {
       asm volatile("" ::"v"(pm[qb]));
-      if (dirty || __builtin_amdgcn_ballot_w64(pm[qb] > kRowSumLimit) != 0) slow_block(qb, sa, valid, n0, masked);
+      if (dirty || __builtin_amdgcn_ballot_w64(pm[qb] > kRowSumLimit) != 0) slow_block(qb, sa, t, n0, masked);
     } else {
       asm volatile("" ::"v"(rs[qb][0]), "v"(rs[qb][1]));
       if (dirty || __builtin_amdgcn_ballot_w64(rs[qb][0] + rs[qb][1] > kRowSumLimit) != 0)
-        slow_block(qb, sa, valid, n0, masked);
+        slow_block(qb, sa, t, n0, masked);
       l_run[qb] += rs[qb][0] + rs[qb][1];
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -664,110 +671,102 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
 #pragma unroll
   for (int db = 0; db < DB; ++db) voff[db][0] += TILEB, voff[db][1] += TILEB;
 
-  int valid_prev = kBN, n0_prev = 0;
+  if (!wave_active) {
+    // a wave without rows in this item takes only its share of the loads and the barriers
+    // (TL: reading each load's entry before the barrier, like the active waves)
+    for (int t = 0; t < nt; ++t) {
+      int e_dma = 0;
+      if constexpr (TL) e_dma = entry(t + 3);
+#pragma unroll
+      for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx, toff_a);
+      WA_WAIT_VMCNT(NLD);
+      barrier();
+      if constexpr (TL) toff_a = uint32_t(e_dma >> 1) * row_bytes;
+      else toff_a = tile_off(t + 3);
+#pragma unroll
+      for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no DMA may still write this block's LDS at exit
+    return;
+  }
+  int n0_prev = 0;
   int nd = 0;                // next tile that takes the slow path
   bool dirty_prev = false;   // block 0's verdict on the previous tile (tile -1: none)
   bool masked_prev = false;
   for (int t = 0; t < nt; ++t) {
     const uint32_t step_k = ring(t + 2) - ring(t + 1);  // slot advance after this tile's reads
     const uint32_t step_v = ring(t + 1) - ring(t);
-    int n0, valid;
+    int n0 = 0;                // TL: first key row of tile t (set after slot 2)
     bool dirty, masked;
     int e_cur = 0, e_dma = 0;  // TL: entries of tile t and of tile t + 3 (read before the barrier)
     if constexpr (TL) {
       e_cur = entry(t);
       e_dma = entry(t + 3);
-      n0 = 0;  // set from e_cur where first needed (after slot 2)
-      valid = kBN;
       dirty = masked = false;
     } else {
-      int nend;
-      tile_range(t, n0, nend);
-      valid = nend - n0;
       dirty = t == nd;
       if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
       masked = false;  // (TL only: without tile lists the slow path masks by segment end)
     }
 
-    if (__builtin_expect(wave_active, 1)) {
-      // slot 0.  The K fragments it reads were loaded in slot 3 of the previous tile, long
-      // done: one wait for all of them instead of one per matrix op.
-      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
-      __builtin_amdgcn_sched_barrier(0);
-      s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
-        stage_at(1, s1, 8, NS, i);
-        if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)), toff_a);
-      });
-      check_block(1, s1, valid_prev, n0_prev, dirty_prev, masked_prev);
-      // slot 1
-      rs[0][0] = rs[0][1] = 0.f;
-      pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
-        if (i < NPV) {
-          read_v(2 * i);
-          read_v(2 * i + 1);
-        }
-        stage_at(0, s0, 0, NP, i);
-      });
-#pragma unroll
-      for (int db = 0; db < DB; ++db) voff[db][0] += step_v, voff[db][1] += step_v;
-      // slot 2
-      s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
-      if constexpr (TL) {
-        const int e = __builtin_amdgcn_readfirstlane(e_cur);
-        n0 = e >> 1;
-        masked = (e & 1) != 0;
-        dirty = t == 0 || masked;
+    // slot 0.  The K fragments it reads were loaded in slot 3 of the previous tile, long
+    // done: one wait for all of them instead of one per matrix op.
+    __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+    __builtin_amdgcn_sched_barrier(0);
+    s_slot(0, s0, true, [&](int i) __attribute__((always_inline)) {
+      stage_at(1, s1, 8, NS, i);
+      if (i < NS && i % (NS / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NS / (NLD / 2)), toff_a);
+    });
+    check_block(1, s1, t - 1, n0_prev, dirty_prev, masked_prev);
+    // slot 1
+    rs[0][0] = rs[0][1] = 0.f;
+    pv_slot(1, true, [&](int i) __attribute__((always_inline)) {
+      if (i < NPV) {
+        read_v(2 * i);
+        read_v(2 * i + 1);
       }
-      check_block(0, s0, valid, n0, dirty, masked);
-    } else {
+      stage_at(0, s0, 0, NP, i);
+    });
 #pragma unroll
-      for (int idx = NLD / 2; idx < NLD; ++idx) dma_load(t + 2, idx, toff_a);
-    }
-
+    for (int db = 0; db < DB; ++db) voff[db][0] += step_v, voff[db][1] += step_v;
+    // slot 2
+    s_slot(1, s1, true, [&](int i) __attribute__((always_inline)) { stage_at(0, s0, 8, NS, i); });
     if constexpr (TL) {
-      if (!wave_active) {  // the active waves set these before their slow-path check
-        const int e = __builtin_amdgcn_readfirstlane(e_cur);
-        n0 = e >> 1;
-        masked = (e & 1) != 0;
-        dirty = t == 0 || masked;
-      }
+      const int e = __builtin_amdgcn_readfirstlane(e_cur);
+      n0 = e >> 1;
+      masked = (e & 1) != 0;
+      dirty = t == 0 || masked;
     }
+    check_block(0, s0, t, n0, dirty, masked);
+
     WA_WAIT_VMCNT(NLD);  // tile t+1 has landed (tile t+2 may still be in flight) ...
     barrier();           // ... for every wave
     if constexpr (TL) toff_a = uint32_t(e_dma >> 1) * row_bytes;
     else toff_a = tile_off(t + 3);
 
-    if (__builtin_expect(wave_active, 1)) {
-      // slot 3 (after the last tile the K reads hit a buffer nobody uses)
-      rs[1][0] = rs[1][1] = 0.f;
-      pv_slot(0, true, [&](int i) __attribute__((always_inline)) {
-        if (i < NPV) {
+    // slot 3 (after the last tile the K reads hit a buffer nobody uses)
+    rs[1][0] = rs[1][1] = 0.f;
+    pv_slot(0, true, [&](int i) __attribute__((always_inline)) {
+      if (i < NPV) {
 #pragma unroll
-          for (int r = 0; r < 2 * KS / NPV; ++r) read_k(i * (2 * KS / NPV) + r);
-          if (i % (NPV / (NLD / 2)) == 0) dma_load(t + 3, i / (NPV / (NLD / 2)), toff_a);
-        }
-        stage_at(1, s1, 0, NP, i);
-      });
+        for (int r = 0; r < 2 * KS / NPV; ++r) read_k(i * (2 * KS / NPV) + r);
+        if (i % (NPV / (NLD / 2)) == 0) dma_load(t + 3, i / (NPV / (NLD / 2)), toff_a);
+      }
+      stage_at(1, s1, 0, NP, i);
+    });
 #pragma unroll
-      for (int st = 0; st < KS; ++st) koff[st] += step_k;
-    } else {
-#pragma unroll
-      for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
-    }
-    valid_prev = valid;
+    for (int st = 0; st < KS; ++st) koff[st] += step_k;
     n0_prev = n0;
     dirty_prev = dirty;
     masked_prev = masked;
   }
   __builtin_amdgcn_s_waitcnt(kVmcnt0);  // no DMA may still write this block's LDS at exit
-  if (wave_active) {  // block 1 of the last tile
-    s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { stage_at(1, s1, 8, NS, i); });
-    check_block(1, s1, valid_prev, n0_prev, dirty_prev, masked_prev);
-    pv_slot(1, true, [&](int) __attribute__((always_inline)) {});
-  }
+  // block 1 of the last tile
+  s_slot(0, s0, false, [&](int i) __attribute__((always_inline)) { stage_at(1, s1, 8, NS, i); });
+  check_block(1, s1, nt - 1, n0_prev, dirty_prev, masked_prev);
+  pv_slot(1, true, [&](int) __attribute__((always_inline)) {});
 #undef WA_WAIT_VMCNT
 
-  if (!wave_active) return;
   // ---- Output.  A lane holds 4-column pieces of its row spread over the row, so direct
   // stores would write 32 rows per instruction in 8- or 16-byte pieces.  Each 32-row block
   // goes through this wave's LDS staging area instead (16-byte chunks XOR-swizzled by row)
