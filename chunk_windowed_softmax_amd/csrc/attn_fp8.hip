@@ -214,6 +214,12 @@ void attn_fp8_kernel(Fp8Params p) {
     tile_range(u < nt ? u : nt - 1, n0, nend);
     return uint32_t(n0) * row_bytes;
   };
+  // Row offset of tile u from that of tile u - 1 (u >= 1): the next 64 rows, the start of
+  // segment 1 at its first tile, and past the last tile the last tile again.
+  const uint32_t tile_step = 64 * row_bytes, seg1_off = uint32_t(it.kv1_begin) * row_bytes;
+  auto next_off = [&](int u, uint32_t prev) __attribute__((always_inline)) -> uint32_t {
+    return u >= nt ? prev : u == nt0 ? seg1_off : prev + tile_step;
+  };
   const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
   // load `idx` (slice idx / 2; K for even idx, V for odd) of the tile at row offset `toff`
   // into ring slot u % kNBUF.  Issued as asm so that the compiler does not make every LDS read
@@ -278,8 +284,8 @@ void attn_fp8_kernel(Fp8Params p) {
     float x[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sa[b][e + j], c2, -mc[qb]));
-    const int y = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], pb[qb][w], false);
-    pb[qb][w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], y, true);
+    const int y = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pb[qb][w], true);
+    pb[qb][w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], y, false);
   };
   // Slow path of block qb's tile: mask keys past the segment end (and, for causal items,
   // after the lane's own row), tile max, per-row raise of the running max, weights again.
@@ -345,9 +351,11 @@ void attn_fp8_kernel(Fp8Params p) {
     __builtin_amdgcn_sched_barrier(0);
     if (pk_k >= 0) {
       const float* f = fb[pk_k & 1];
-      // (both halves of the word are written: its old contents only save a move)
-      const int y = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], pb[qb][pk_k], false);
-      pb[qb][pk_k] = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], y, true);
+      // (both halves of the word are written: its old contents only save a move).  The high
+      // half first: a write of the high half needs a wait state before the next instruction
+      // on gfx950, the low half does not.
+      const int y = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pb[qb][pk_k], true);
+      pb[qb][pk_k] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], y, false);
       pm[qb] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(pm[qb], f[0]), f[1]), f[2]), f[3]);
       asm volatile("" ::"v"(pb[qb][pk_k]), "v"(pm[qb]));
     }
@@ -472,7 +480,7 @@ void attn_fp8_kernel(Fp8Params p) {
       for (int idx = kNLD / 2; idx < kNLD; ++idx) dma_load(t + 2, idx, toff_a);
       __builtin_amdgcn_s_waitcnt(0x0F70 | kNLD);
       barrier();
-      toff_a = tile_off(t + 3);
+      toff_a = next_off(t + 3, toff_a);
 #pragma unroll
       for (int idx = 0; idx < kNLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
     }
@@ -510,7 +518,7 @@ void attn_fp8_kernel(Fp8Params p) {
     check_block(0, s0, t, dirty);
     __builtin_amdgcn_s_waitcnt(0x0F70 | kNLD);  // tile t+1 has landed (t+2 may be in flight) ...
     barrier();                                   // ... for every wave
-    toff_a = tile_off(t + 3);
+    toff_a = next_off(t + 3, toff_a);
     // slot 3 (after the last tile the K reads hit a slot nobody uses)
     pv_slot(0, [&](int i) __attribute__((always_inline)) {
       if (i < 4) {

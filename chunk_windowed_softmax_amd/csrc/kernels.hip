@@ -282,6 +282,12 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   };
   // DMA load `idx` (slice idx / 2, K for even idx and V for odd) of the tile at row offset
   // `toff` into ring slot u % NBUF.
+  // Row offset of tile u from that of tile u - 1 (u >= 1, without tile lists): the next 64
+  // rows, the start of segment 1 at its first tile, and past the last tile the last tile again.
+  const uint32_t tile_step = kBN * row_bytes, seg1_off = uint32_t(it.kv1_begin) * row_bytes;
+  auto next_off = [&](int u, uint32_t prev) __attribute__((always_inline)) -> uint32_t {
+    return u >= nt ? prev : u == nt0 ? seg1_off : prev + tile_step;
+  };
   const uint32_t lds_base = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)smem));
   auto dma_load = [&](int u, int idx, uint32_t toff) __attribute__((always_inline)) {
     const int i = idx >> 1;
@@ -682,7 +688,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
       WA_WAIT_VMCNT(NLD);
       barrier();
       if constexpr (TL) toff_a = uint32_t(e_dma >> 1) * row_bytes;
-      else toff_a = tile_off(t + 3);
+      else toff_a = next_off(t + 3, toff_a);
 #pragma unroll
       for (int idx = 0; idx < NLD / 2; ++idx) dma_load(t + 3, idx, toff_a);
     }
@@ -742,7 +748,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
     WA_WAIT_VMCNT(NLD);  // tile t+1 has landed (tile t+2 may still be in flight) ...
     barrier();           // ... for every wave
     if constexpr (TL) toff_a = uint32_t(e_dma >> 1) * row_bytes;
-    else toff_a = tile_off(t + 3);
+    else toff_a = next_off(t + 3, toff_a);
 
     // slot 3 (after the last tile the K reads hit a buffer nobody uses)
     rs[1][0] = rs[1][1] = 0.f;
