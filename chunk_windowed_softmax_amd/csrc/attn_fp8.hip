@@ -396,29 +396,44 @@ void attn_fp8_kernel(Fp8Params p) {
     return n;
   };
   const f32x16 zero = {};
+  // A matrix op leads its step (a scheduling barrier keeps the step's vector work after it),
+  // except in the last step of a slot, where it follows the vector work: issued last, it
+  // runs on through the slot boundary (the checks, the barrier, the loop's scalar work),
+  // none of which depends on it.
   auto s_slot = [&](int qb, f32x16 (&sa)[2], bool mma, auto&& extra) __attribute__((always_inline)) {
+    auto op = [&](int i) __attribute__((always_inline)) {
+      const int s = i >> 1, b = i & 1;
+      sa[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[s][b], qf[qb][s], s == 0 ? zero : sa[b], 0, 0, 0, 0,
+                                                              0, 0);
+    };
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      if (mma) {
-        const int s = i >> 1, b = i & 1;
-        sa[b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[s][b], qf[qb][s], s == 0 ? zero : sa[b], 0, 0, 0, 0,
-                                                                0, 0);
-      }
-      __builtin_amdgcn_sched_barrier(0);  // the matrix op leads its step
+      if (mma && i < NS - 1) op(i);
+      __builtin_amdgcn_sched_barrier(0);
       extra(i);
       __builtin_amdgcn_sched_barrier(0);
+      if (mma && i == NS - 1) {
+        op(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   auto pv_slot = [&](int qb, auto&& extra) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NP; ++i) {
+    auto op = [&](int i) __attribute__((always_inline)) {
       if (i < 4) oacc[qb][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[i], pb[qb], oacc[qb][i], 0, 0, 0, 0,
                                                                               0, 0);
-      else lacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb[qb], lacc[qb], 0, 0, 0, 0,
-                                                                                 0, 0);
+      else lacc[qb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb[qb], lacc[qb], 0, 0, 0, 0, 0, 0);
+    };
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+      if (i < NP - 1) op(i);
       __builtin_amdgcn_sched_barrier(0);
       extra(i);
       __builtin_amdgcn_sched_barrier(0);
+      if (i == NP - 1) {
+        op(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
   auto barrier = [&]() __attribute__((always_inline)) {
