@@ -179,7 +179,8 @@ def bench_fp8(args, w) -> int:
     achieved = flop / (dev_ms * 1e-3) / 1e12
     traffic, traffic_rec = recorded_traffic(w.name, "attn_fp8_kernel")
     res = {
-        "metric": "kept-pair TFLOP/s of the FP8 (e4m3) window call at the H3-scale share on 1 MI355X",
+        "metric": ("kept-pair TFLOP/s of the FP8 (e4m3) window call at the H3-scale share on 1 MI355X"
+                   if w.name.startswith("h3") else f"kept-pair TFLOP/s of the FP8 (e4m3) {w.name} call on 1 MI355X"),
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
