@@ -349,15 +349,17 @@ void attn_fp8_kernel(Fp8Params p) {
       if (fe_k == 0) pm[qb] = 0.f;
     }
     __builtin_amdgcn_sched_barrier(0);
+    // Packing of word pk_k to e4m3, in two halves around the exponentials of word fe_k: on
+    // gfx950 an instruction that reads the result of a v_cvt_pk_fp8_f32 writing the high
+    // half of its register needs a wait state, which the exponentials fill.  (Both halves
+    // of the word are written: its old contents only save a move.)
+    int y = 0;
     if (pk_k >= 0) {
       const float* f = fb[pk_k & 1];
-      // (both halves of the word are written: its old contents only save a move).  The high
-      // half first: a write of the high half needs a wait state before the next instruction
-      // on gfx950, the low half does not.
-      const int y = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pb[qb][pk_k], true);
-      pb[qb][pk_k] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], y, false);
       pm[qb] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(pm[qb], f[0]), f[1]), f[2]), f[3]);
-      asm volatile("" ::"v"(pb[qb][pk_k]), "v"(pm[qb]));
+      asm volatile("" ::"v"(pm[qb]));
+      y = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pb[qb][pk_k], true);
+      asm volatile("" ::"v"(y));
     }
     __builtin_amdgcn_sched_barrier(0);
     if (fe_k >= 0) {
@@ -365,6 +367,12 @@ void attn_fp8_kernel(Fp8Params p) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_exp2f(f[j]);
       asm volatile("" ::"v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (pk_k >= 0) {
+      const float* f = fb[pk_k & 1];
+      pb[qb][pk_k] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], y, false);
+      asm volatile("" ::"v"(pb[qb][pk_k]));
     }
   };
   auto pin_p = [&](int qb) __attribute__((always_inline)) {
