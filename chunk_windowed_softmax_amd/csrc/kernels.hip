@@ -25,10 +25,14 @@
 //   read from LDS feeds the matrix ops of both 32-row blocks.
 //   Softmax runs in the log2 domain (exp2 with log2(e)/sqrt(d) folded into one FMA),
 //   online over 64-key tiles with fp32 running max / sum / accumulators.
-//   The matrix ops of one tile come in four groups of 16 (S of block 0, PV of block 1 for
-//   the previous tile, S of block 1, PV of block 0); the exponentials, bf16 packing and
-//   row sums of the other block, and the LDS reads of the next fragments, are interleaved
-//   one matrix op at a time, so the vector ALU and LDS work hides under the matrix pipe.
+//   The matrix ops of one tile come in four groups (S of block 0, PV of block 1 for the
+//   previous tile, S of block 1, PV of block 0; 16 each at d = 128); the exponentials, bf16
+//   packing and row sums of the other block, and the LDS reads of the next fragments, are
+//   interleaved one matrix op at a time, so the vector ALU and LDS work hides under the
+//   matrix pipe.  At d = 64, where the vector ALU is the bound, the row sums are four more
+//   matrix ops per PV group against an all-ones operand instead.
+//   A wave whose rows lie past the end of an item runs a loop of its own that only takes
+//   its share of the tile loads and the barriers.
 //   K/V tiles stream through a 4-deep LDS ring filled by direct global->LDS 16-byte loads
 //   (no registers, no LDS write instructions), issued three tiles ahead and spread over
 //   the matrix ops; one barrier per tile.  The loads go through range-checked buffer
