@@ -40,9 +40,29 @@ COPY = "copyBuffer"
 SOURCES = {ATTN: "kernels.hip", PROLOGUE: "prologue.hip", FP8: "attn_fp8.hip"}
 
 
+def _code_only(text: str) -> str:
+    """The source without its comments and with runs of whitespace collapsed, so that
+    counters stay tied to the code they were taken on across comment edits.  (The kernel
+    sources hold no string or character literal with a comment marker in it.)"""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        if text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(text[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_sha256(kernel: str = ATTN) -> str:
-    with open(os.path.join(PKG, "csrc", SOURCES[kernel]), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of the kernel's source file, comments and whitespace runs removed."""
+    with open(os.path.join(PKG, "csrc", SOURCES[kernel]), encoding="utf-8") as f:
+        return hashlib.sha256(_code_only(f.read()).encode()).hexdigest()
 
 
 def _rows(pattern: str) -> List[Dict[str, str]]:
@@ -223,7 +243,7 @@ def main() -> int:
         f"Traffic per launch {res['traffic_bytes']:.4g} B vs algorithmic {a.algorithmic_bytes:.4g} B "
         f"(ratio {res['traffic_bytes'] / a.algorithmic_bytes:.2f}); {res['hbm_gbs_at_avg_duration']:.0f} GB/s.",
         "",
-        f"Kernel source sha256: `{res['kernel_source_sha256']}`",
+        f"Kernel source sha256 (comments and whitespace runs removed): `{res['kernel_source_sha256']}`",
         "",
     ] + sq_lines
     with open(a.out + ".md", "w") as f:
