@@ -32,7 +32,9 @@
 //   matrix pipe.  At d = 64, where the vector ALU is the bound, the row sums are four more
 //   matrix ops per PV group against an all-ones operand instead.
 //   A wave whose rows lie past the end of an item runs a loop of its own that only takes
-//   its share of the tile loads and the barriers.
+//   its share of the tile loads and the barriers.  An item of at most 64 rows (d = 128; at
+//   H3 the last rows of every group) is instead split over all four waves: 32 rows and one
+//   32-key half of every tile each, the halves merged by log-sum-exp through the LDS.
 //   K/V tiles stream through a 4-deep LDS ring filled by direct global->LDS 16-byte loads
 //   (no registers, no LDS write instructions), issued three tiles ahead and spread over
 //   the matrix ops; one barrier per tile.  The loads go through range-checked buffer
@@ -164,6 +166,9 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   // half the matrix work of d = 128 and the same vector work, so the vector ALU is the
   // bound and the trade pays; at d = 128 the matrix pipe is the busier one and it would not.
   constexpr bool ONES = D == 64;
+  // Items of at most 64 rows run split over the four waves by key half (d = 128, window
+  // and global-leg items without tile lists; see the split-item loop below).
+  constexpr bool kSplitItems = !ONES && !TL;
 
   constexpr int NBUF = 4;                       // LDS ring of (K, V) tile pairs
   constexpr int RINGB = NBUF * 2 * TILEB;       // bytes of the ring
@@ -644,6 +649,320 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   // s_waitcnt with vmcnt = n (n < 16) and the other counters at their maximum
 #define WA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(0x0F70 | (n))
 
+  // ---- Output of the 32-row block qb (rows r0 ..): a lane holds 4-column pieces of its row
+  // spread over the row, so direct stores would write 32 rows per instruction in 8- or
+  // 16-byte pieces.  The block goes through this wave's LDS staging area instead (16-byte
+  // chunks XOR-swizzled by row) and leaves as whole rows: 16 lanes x 16 bytes per 256 bytes
+  // of a row.  Global-leg items write the fp32 partial result (O, max, sum) instead.
+  auto output_block = [&](int qb, int r0) __attribute__((always_inline)) {
+    unsigned char* const stage = smem + RINGB + wave * STAGEB;
+    const bool partial = it.split >= 0;
+    // Lane indices redefined here (empty asm) so that the staging addresses, which depend
+    // only on them, are computed here and not hoisted out of the unit loop into the tile
+    // loop's register budget.
+    int orow_l = l32, olane = lane;
+    asm volatile("" : "+v"(orow_l), "+v"(olane));
+    constexpr int EB = OUT_F32 ? 4 : 2;  // bytes per element of the final output
+    const float l_tot = ONES ? lacc[qb][0] : [&] {
+      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, l_run[qb]),
+                                                      __builtin_bit_cast(uint32_t, l_run[qb]), false, false);
+      return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+    }();
+    const int rows_here = it.q_end - r0;  // valid rows of this block (may be <= 0)
+    if (rows_here <= 0) return;
+
+    auto emit = [&](auto eb_c, auto row_dst) __attribute__((always_inline)) {
+      constexpr int E = decltype(eb_c)::value;       // bytes per element
+      constexpr int RB = D * E;                      // bytes per output row
+      constexpr int CR = (RB < 256 ? RB : 256) / 16;  // 16-byte chunks per row per round
+      constexpr int ROUNDS = RB / (CR * 16);
+      static_assert(32 * CR * 16 <= STAGEB, "one round of 32 rows fits the staging area");
+      const float mul = 1.f / l_tot;
+#pragma unroll
+      for (int rd = 0; rd < ROUNDS; ++rd) {
+        // write: the lane's 4-element pieces of row l32 that fall in this round
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int off = (32 * db + 8 * g4) * E + (E == 2 ? 8 : 16) * hh - rd * CR * 16;  // byte offset in the round
+            if (off < 0 || off >= CR * 16) continue;
+            const int c = off >> 4, within = off & 15;
+            unsigned char* dst = stage + orow_l * (CR * 16) + ((c ^ (orow_l & (CR - 1))) << 4) + within;
+            const float v0 = oacc[qb][db][4 * g4] * mul, v1 = oacc[qb][db][4 * g4 + 1] * mul;
+            const float v2 = oacc[qb][db][4 * g4 + 2] * mul, v3 = oacc[qb][db][4 * g4 + 3] * mul;
+            if constexpr (E == 2) {
+              *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            } else {
+              *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
+            }
+          }
+        // read back whole chunks in row order and store them
+#pragma unroll
+        for (int k = 0; k < 32 * CR / 64; ++k) {
+          const int j = k * 64 + olane, r = j / CR, c = j % CR;
+          const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (CR * 16) + ((c ^ (r & (CR - 1))) << 4));
+          if (r < rows_here) *reinterpret_cast<u32x4*>(row_dst(r0 + r) + rd * CR * 16 + c * 16) = x;
+        }
+      }
+    };
+    if (!partial) {
+      emit(std::integral_constant<int, EB>{}, [&](int qrow) __attribute__((always_inline)) {
+        return reinterpret_cast<unsigned char*>(p.out) + ((int64_t)qrow * H + h) * D * EB;
+      });
+    } else {
+      const int qrow = r0 + l32;
+      if (qrow < it.q_end) {
+        const int64_t slot = ((int64_t)it.split * p.G + (qrow - p.frame_rows)) * H + h;
+        float* po = p.part_o + slot * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dv = 32 * db + 8 * g4 + 4 * hh;
+            const f32x4 o = {oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
+                             oacc[qb][db][4 * g4 + 3]};
+            *reinterpret_cast<f32x4*>(po + dv) = o;
+          }
+        if (hh == 0) {
+          const float2 ml = make_float2(m_run[qb] * c2, l_tot);
+          *reinterpret_cast<float2*>(p.part_ml + slot * 2) = ml;
+        }
+      }
+    }
+  };
+
+  // ---- Items of at most one wave's rows (at H3 the last 64 rows of every 2880-row group):
+  // run as above, one wave would work while three SIMDs idle.  Here every wave takes one
+  // 32-row block (qs = wave & 1) and one 32-key half (kh = wave >> 1) of every tile, with the
+  // same ring, loads and barriers; the two key halves of a block merge by log-sum-exp through
+  // the LDS at the end.  Per tile two slots of KS matrix ops:
+  //   slot A: S(t) = K(t) Q^T (this key half)  | P(t-1) pairs 4..7, second half of the DMA
+  //                                             of t+2; then the slow path of tile t-1 if
+  //                                             due (as above, over this wave's 16 keys per row)
+  //   barrier: tile t+1 has landed for every wave
+  //   slot B: O += V(t-1)^T P(t-1)^T          | P(t) pairs 0..3, V(t) reads (each right
+  //                                             after its fragment's last use), K(t+1)
+  //                                             reads, first half of the DMA of t+3
+  // S, P and the row sums of a tile alternate between two register sets (tile t's are
+  // written while tile t-1's are still read), so the tile loop is unrolled twice.
+  if constexpr (kSplitItems) {
+    if (!causal && it.q_end - it.q_begin <= kWaveRows) {
+      const int qs = wave & 1, kh = wave >> 1;
+      const int r0q = it.q_begin + 32 * qs;
+      constexpr int NQ = KS;  // matrix ops of either slot (= 2 * DB)
+      static_assert(NQ == 2 * DB && NQ % (NLD / 2) == 0 && NQ % 8 == 0, "split-item slots");
+      f32x16(&sq)[2] = s0;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) koff[s] += uint32_t(kh * 32 * ROWB);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) voff[db][0] += uint32_t(kh * 32 * ROWB), voff[db][1] += uint32_t(kh * 32 * ROWB);
+      {
+        const uint32_t toff0 = tile_off(0);
+#pragma unroll
+        for (int idx = 0; idx < NLD; ++idx) dma_load(0, idx, toff0);
+      }
+      {
+        const int qrow = r0q + l32;
+        const bool ok = qrow < it.q_end;
+        const uint16_t* src = p.q + ((int64_t)qrow * H + h) * D + 8 * hh;
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          u32x4 x = {0u, 0u, 0u, 0u};
+          if (ok) x = *reinterpret_cast<const u32x4*>(src + 16 * s);
+          qf[0][s] = __builtin_bit_cast(bf16x8, x);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
+      uint32_t toff_q = tile_off(1);
+#pragma unroll
+      for (int idx = 0; idx < NLD; ++idx) dma_load(1, idx, toff_q);
+      toff_q = tile_off(2);
+#pragma unroll
+      for (int idx = 0; idx < NLD / 2; ++idx) dma_load(2, idx, toff_q);
+      barrier();
+#pragma unroll
+      for (int s = 0; s < KS; ++s) read_k(2 * s);
+#pragma unroll
+      for (int st = 0; st < KS; ++st) koff[st] += ring(1);
+#pragma unroll
+      for (int db = 0; db < DB; ++db) voff[db][0] += TILEB, voff[db][1] += TILEB;
+
+      // pairs lo .. lo+3 of P into register set `buf` at step i of a slot: pair k's FMA at
+      // step (k - lo) * NQ / 4, exp2 one step later, packing the step after, row sum (v_dot2)
+      // the step after that
+      constexpr int kTailQ = 3 * NQ / 4 + 4 - NQ;
+      auto stage_q = [&](int buf, int lo, int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = lo; k < lo + 4; ++k) {
+          const int fs = (k - lo) * NQ / 4;
+          if (fs + 3 == i) dot_pair(buf, k, pw[buf][k]);
+          if (fs + 2 == i) {
+            pw[buf][k] = cvt_bf16x2(fa[k], fb[k]);
+            asm volatile("" ::"v"(pw[buf][k]));
+          }
+          if (fs + 1 == i) {
+            fa[k] = fast_exp2(fa[k]);
+            fb[k] = fast_exp2(fb[k]);
+            asm volatile("" ::"v"(fa[k]), "v"(fb[k]));
+          }
+          if (fs == i) {
+            fa[k] = __builtin_fmaf(sq[buf][2 * k], c2, -mc[0]);
+            fb[k] = __builtin_fmaf(sq[buf][2 * k + 1], c2, -mc[0]);
+            asm volatile("" ::"v"(fa[k]), "v"(fb[k]));
+          }
+        }
+      };
+      // slow path of tile t: mask keys past the segment end, raise the max of rows whose max
+      // grew by more than 2^8, recompute P(t) into `buf`
+      auto slow_q = [&](int buf, int t) __attribute__((always_inline)) {
+        int k0, kend;
+        tile_range(t, k0, kend);
+        const int valid = kend - k0;
+        if (valid < kBN) {
+          const int lim = valid - 32 * kh - 4 * hh;  // key (32*kh + (i/4)*8 + 4*hh + i%4) >= valid
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sq[buf][i] = ((i >> 2) * 8 + (i & 3)) >= lim ? -__builtin_inff() : sq[buf][i];
+        }
+        float mt = sq[buf][0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, sq[buf][i]);
+        mt = pair_max(mt);
+        const bool grow = mt > m_run[0] + lazy_raw;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+          const float m_new = grow ? mt : m_run[0];
+          const float alpha = fast_exp2((m_run[0] - m_new) * c2);
+          m_run[0] = m_new;
+          mc[0] = m_new * c2;
+          l_run[0] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) oacc[0][db][i] *= alpha;
+        }
+        rs[buf][0] = rs[buf][1] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          pw[buf][k] = cvt_bf16x2(fast_exp2(__builtin_fmaf(sq[buf][2 * k], c2, -mc[0])),
+                                  fast_exp2(__builtin_fmaf(sq[buf][2 * k + 1], c2, -mc[0])));
+          add_pair(buf, pw[buf][k]);
+        }
+      };
+      // slot B's matrix op i: O += V^T P^T for (16-key piece tt, 32 columns db) of the tile
+      auto pv_q = [&](int buf, int i) __attribute__((always_inline)) {
+        const int tt = i / DB, db = i % DB;
+        oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(0, tt, db), pfrag(buf, 0, tt), oacc[0][db], 0, 0, 0);
+      };
+      // tile t-1's verdict, with its pairs complete (register set `buf`)
+      auto check_q = [&](int buf, int t, bool dirty) __attribute__((always_inline)) {
+        asm volatile("" ::"v"(pw[buf][0]), "v"(pw[buf][1]), "v"(pw[buf][2]), "v"(pw[buf][3]), "v"(pw[buf][4]),
+                     "v"(pw[buf][5]), "v"(pw[buf][6]), "v"(pw[buf][7]), "v"(rs[buf][0]), "v"(rs[buf][1]));
+        if (dirty || __builtin_amdgcn_ballot_w64(rs[buf][0] + rs[buf][1] > kRowSumLimit) != 0) slow_q(buf, t);
+        l_run[0] += rs[buf][0] + rs[buf][1];
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      int nd = 0;               // next tile that takes the slow path
+      bool dirty_prev = false;  // verdict input of tile t-1 (tile -1: none)
+      // tile -1 (register set 1): scores -inf, so its weights, row sums and PV are zero
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sq[1][i] = -__builtin_inff();
+      rs[1][0] = rs[1][1] = 0.f;
+      auto tile_q = [&](int t, auto cur_c) __attribute__((always_inline)) {
+        constexpr int cur = decltype(cur_c)::value, prv = cur ^ 1;  // register sets of tiles t, t-1
+        const uint32_t step_k = ring(t + 2) - ring(t + 1);
+        const uint32_t step_v = ring(t + 1) - ring(t);
+        const bool dirty = t == nd;
+        if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
+        __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+        __builtin_amdgcn_sched_barrier(0);
+        // slot A
+#pragma unroll
+        for (int i = 0; i < NQ + kTailQ; ++i) {
+          if (i < NQ) {
+            sq[cur] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[i][0], qf[0][i], i == 0 ? zero : sq[cur], 0, 0, 0);
+            if (i % (NQ / (NLD / 2)) == 0) dma_load(t + 2, NLD / 2 + i / (NQ / (NLD / 2)), toff_q);
+          }
+          stage_q(prv, 4, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        check_q(prv, t - 1, dirty_prev);
+        WA_WAIT_VMCNT(NLD);  // tile t+1 has landed (tile t+2 may still be in flight) ...
+        barrier();           // ... for every wave
+        toff_q = next_off(t + 3, toff_q);
+        // slot B
+        rs[cur][0] = rs[cur][1] = 0.f;
+#pragma unroll
+        for (int i = 0; i < NQ + kTailQ; ++i) {
+          if (i < NQ) {
+            pv_q(prv, i);
+            read_v(2 * i);
+            read_v(2 * i + 1);
+            read_k(2 * i);
+            if (i % (NQ / (NLD / 2)) == 0) dma_load(t + 3, i / (NQ / (NLD / 2)), toff_q);
+          }
+          stage_q(cur, 0, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) voff[db][0] += step_v, voff[db][1] += step_v;
+#pragma unroll
+        for (int st = 0; st < KS; ++st) koff[st] += step_k;
+        dirty_prev = dirty;
+      };
+      for (int t = 0; t < nt; t += 2) {
+        tile_q(t, std::integral_constant<int, 0>{});
+        if (t + 1 < nt) tile_q(t + 1, std::integral_constant<int, 1>{});
+      }
+      // the last tile: its pairs 4..7, its verdict, its PV
+      auto last_q = [&](auto buf_c) __attribute__((always_inline)) {
+        constexpr int buf = decltype(buf_c)::value;
+#pragma unroll
+        for (int i = 0; i < NQ + kTailQ; ++i) {
+          stage_q(buf, 4, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        check_q(buf, nt - 1, dirty_prev);
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) pv_q(buf, i);
+      };
+      if ((nt - 1) & 1) last_q(std::integral_constant<int, 1>{});
+      else last_q(std::integral_constant<int, 0>{});
+      // merge the key halves: the kh = 1 wave of each block leaves O (64 floats per lane, in
+      // lane order, conflict free) and its (max, sum) in the idle ring; the kh = 0 wave, whose
+      // lanes own the same rows and columns, merges them and writes the block
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the ring's last loads have landed ...
+      barrier();                            // ... and no wave reads it any more
+      unsigned char* const mb = smem + qs * (DB * 4 * 1024 + 512);
+      if (kh == 1) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f32x4*>(mb + (db * 4 + g4) * 1024 + lane * 16) =
+                f32x4{oacc[0][db][4 * g4], oacc[0][db][4 * g4 + 1], oacc[0][db][4 * g4 + 2], oacc[0][db][4 * g4 + 3]};
+        *reinterpret_cast<f32x2*>(mb + DB * 4 * 1024 + lane * 8) = f32x2{m_run[0], l_run[0]};
+      }
+      barrier();
+      if (kh == 0) {
+        const f32x2 ml = *reinterpret_cast<const f32x2*>(mb + DB * 4 * 1024 + lane * 8);
+        const float m_new = __builtin_fmaxf(m_run[0], ml[0]);
+        const float a0 = fast_exp2((m_run[0] - m_new) * c2), a1 = fast_exp2((ml[0] - m_new) * c2);
+        m_run[0] = m_new;
+        l_run[0] = l_run[0] * a0 + ml[1] * a1;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 x = *reinterpret_cast<const f32x4*>(mb + (db * 4 + g4) * 1024 + lane * 16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) oacc[0][db][4 * g4 + j] = oacc[0][db][4 * g4 + j] * a0 + x[j] * a1;
+          }
+        output_block(0, r0q);
+      }
+      return;
+    }
+  }
+
   // prologue: tile 0 and the Q fragments land together (the explicit wait also tells the
   // compiler that Q is complete, so it adds no wait inside the loop); then tiles 1 and the
   // first half of 2 go in flight.
@@ -777,87 +1096,8 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   pv_slot(1, true, [&](int) __attribute__((always_inline)) {});
 #undef WA_WAIT_VMCNT
 
-  // ---- Output.  A lane holds 4-column pieces of its row spread over the row, so direct
-  // stores would write 32 rows per instruction in 8- or 16-byte pieces.  Each 32-row block
-  // goes through this wave's LDS staging area instead (16-byte chunks XOR-swizzled by row)
-  // and leaves as whole rows: 16 lanes x 16 bytes per 256 bytes of a row.
-  unsigned char* const stage = smem + RINGB + wave * STAGEB;
-  const bool partial = it.split >= 0;
-  // Lane indices redefined here (empty asm) so that the staging addresses, which depend only
-  // on them, are computed here and not hoisted out of the unit loop into the tile loop's
-  // register budget.
-  int orow_l = l32, olane = lane;
-  asm volatile("" : "+v"(orow_l), "+v"(olane));
-  constexpr int EB = OUT_F32 ? 4 : 2;  // bytes per element of the final output
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const float l_tot = ONES ? lacc[qb][0] : [&] {
-      const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, l_run[qb]),
-                                                      __builtin_bit_cast(uint32_t, l_run[qb]), false, false);
-      return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
-    }();
-    const int rows_here = it.q_end - (row0 + 32 * qb);  // valid rows of this block (may be <= 0)
-    if (rows_here <= 0) continue;
-    auto emit = [&](auto eb_c, auto row_dst) __attribute__((always_inline)) {
-      constexpr int E = decltype(eb_c)::value;       // bytes per element
-      constexpr int RB = D * E;                      // bytes per output row
-      constexpr int CR = (RB < 256 ? RB : 256) / 16;  // 16-byte chunks per row per round
-      constexpr int ROUNDS = RB / (CR * 16);
-      static_assert(32 * CR * 16 <= STAGEB, "one round of 32 rows fits the staging area");
-      const float mul = 1.f / l_tot;
-#pragma unroll
-      for (int rd = 0; rd < ROUNDS; ++rd) {
-        // write: the lane's 4-element pieces of row l32 that fall in this round
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int off = (32 * db + 8 * g4) * E + (E == 2 ? 8 : 16) * hh - rd * CR * 16;  // byte offset in the round
-            if (off < 0 || off >= CR * 16) continue;
-            const int c = off >> 4, within = off & 15;
-            unsigned char* dst = stage + orow_l * (CR * 16) + ((c ^ (orow_l & (CR - 1))) << 4) + within;
-            const float v0 = oacc[qb][db][4 * g4] * mul, v1 = oacc[qb][db][4 * g4 + 1] * mul;
-            const float v2 = oacc[qb][db][4 * g4 + 2] * mul, v3 = oacc[qb][db][4 * g4 + 3] * mul;
-            if constexpr (E == 2) {
-              *reinterpret_cast<u32x2*>(dst) = u32x2{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-            } else {
-              *reinterpret_cast<f32x4*>(dst) = f32x4{v0, v1, v2, v3};
-            }
-          }
-        // read back whole chunks in row order and store them
-#pragma unroll
-        for (int k = 0; k < 32 * CR / 64; ++k) {
-          const int j = k * 64 + olane, r = j / CR, c = j % CR;
-          const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (CR * 16) + ((c ^ (r & (CR - 1))) << 4));
-          if (r < rows_here) *reinterpret_cast<u32x4*>(row_dst(row0 + 32 * qb + r) + rd * CR * 16 + c * 16) = x;
-        }
-      }
-    };
-    if (!partial) {
-      emit(std::integral_constant<int, EB>{}, [&](int qrow) __attribute__((always_inline)) {
-        return reinterpret_cast<unsigned char*>(p.out) + ((int64_t)qrow * H + h) * D * EB;
-      });
-    } else {
-      const int qrow = row0 + 32 * qb + l32;
-      if (qrow < it.q_end) {
-        const int64_t slot = ((int64_t)it.split * p.G + (qrow - p.frame_rows)) * H + h;
-        float* po = p.part_o + slot * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dv = 32 * db + 8 * g4 + 4 * hh;
-            const f32x4 o = {oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
-                             oacc[qb][db][4 * g4 + 3]};
-            *reinterpret_cast<f32x4*>(po + dv) = o;
-          }
-        if (hh == 0) {
-          const float2 ml = make_float2(m_run[qb] * c2, l_tot);
-          *reinterpret_cast<float2*>(p.part_ml + slot * 2) = ml;
-        }
-      }
-    }
-  }
+  for (int qb = 0; qb < 2; ++qb) output_block(qb, row0 + 32 * qb);
   };  // run_item
 
   for (int n = 0;; ++n) {

@@ -246,6 +246,37 @@ def test_score_jump_parity(gpu_lib):
         assert np.abs(got[row].numpy() - v[key].float().numpy()).max() <= 2e-2, row
 
 
+def test_score_jump_short_items(gpu_lib):
+    """Items of at most 64 rows (here a 44-row window item and a 30-row global item) run
+    split over the four waves by key half.  Hot keys in either half of a tile, in a ragged
+    tile at a segment end and among the ragged global keys send those tiles to the slow
+    path of one half; the halves' merge must keep every row one-hot on its key."""
+    # three 300-row groups (chunk spans 0-1, 0-2, 1-2): items of 256 + 44 rows
+    T, S, G, K, r, H, d = 9, 100, 30, 3, 1, 2, 128
+    _say(f"score jump, short items T={T} S={S} G={G} K={K} r={r} H={H} d={d}")
+    L = T * S + G
+    q, k, v = make_custom_inputs(L, H, d, torch.bfloat16, seed=11)
+    hot = ((260, 100),        # group 0's 44-row item: key 36 of tile 1 (second key half)
+           (290, 590),        # key 14 of tile 9, where the chunk keys end after 24 keys
+           (299, 920),        # global key: key 20 of the 30-key global tile
+           (870, 850),        # group 2's 44-row item (keys from 300): key 38 of tile 8
+           (T * S + 5, 300))  # 30-row global item
+    for row, key in hot:
+        _hot_key(q, k, row, key, 10.0)
+    plan = gpu_lib.wa_plan_create(T, S, G, K, r, H, d)
+    out = torch.full((L, H, d), float("nan"), dtype=torch.bfloat16, device="cuda")
+    gpu_lib.wa_forward(plan, q.cuda(), k.cuda(), v.cuda(), out=out)
+    torch.cuda.synchronize()
+    ref = window_attention_reference(q, k, v, Geometry(T, S, G, K, r))
+    got = out.float().cpu()
+    rel, mx = _errors(got, ref)
+    _say(f"rel_l2={rel:.3e} max_abs={mx:.3e}")
+    assert not torch.isnan(got).any()
+    assert rel <= REL_L2 and mx <= MAX_ABS
+    for row, key in hot:
+        assert np.abs(got[row].numpy() - v[key].float().numpy()).max() <= 2e-2, row
+
+
 def test_score_jump_causal(gpu_lib):
     # bf16 inputs: products of exactly representable values, so scores in the hundreds
     # carry no input-rounding error (fp32 inputs would be rounded to bf16 first, and an
