@@ -258,6 +258,7 @@ void attn_fp8_kernel(Fp8Params p) {
   i32x8 vf[4];     // V^T fragments [d-block]
   i32x8 pb[2];     // P^T [qb]: word w = S elements 4 (w % 4) .. +3 of key block w / 4
   float pm[2];     // max weight of the block's current tile (fast path)
+  f32x16 s0_split;  // scores of the split-item path
   pb[1] = i32x8{};
 #pragma unroll
   for (int db = 0; db < 4; ++db) vf[db] = i32x8{};
@@ -453,6 +454,268 @@ void attn_fp8_kernel(Fp8Params p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
+  // ---- Output of the 32-row block qb (rows r0 ..).  A lane holds 4-column pieces of its row
+  // spread over the row; the block goes through this wave's LDS staging area (16-byte chunks
+  // XOR-swizzled by row) and leaves as whole rows, 16 lanes x 16 bytes per row.  Global-leg
+  // partials (fp32, already times scale_v) go straight out.
+  auto output_block = [&](int qb, int r0) __attribute__((always_inline)) {
+    unsigned char* const stage = smem + kRingB + wave * kStageB;
+    // lane indices redefined here (empty asm) so that the staging addresses are computed
+    // here and not hoisted out of the unit loop into the tile loop's register budget
+    int orow_l = l32, olane = lane;
+    asm volatile("" : "+v"(orow_l), "+v"(olane));
+    const int rows_here = it.q_end - r0;
+    if (rows_here <= 0) return;
+    const float l_tot = lacc[qb][0];  // every element holds the row sum over both halves
+    if (it.split < 0) {
+      const float mul = p.scale_v / l_tot;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int off = (32 * db + 8 * g4) * 2 + 8 * hh;  // byte offset in the row
+          unsigned char* dst = stage + orow_l * (kD * 2) + (((off >> 4) ^ (orow_l & 15)) << 4) + (off & 15);
+          *reinterpret_cast<u32x2*>(dst) =
+              u32x2{pack_bf16x2(oacc[qb][db][4 * g4] * mul, oacc[qb][db][4 * g4 + 1] * mul),
+                    pack_bf16x2(oacc[qb][db][4 * g4 + 2] * mul, oacc[qb][db][4 * g4 + 3] * mul)};
+        }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = k * 64 + olane, r = j >> 4, c = j & 15;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (kD * 2) + ((c ^ (r & 15)) << 4));
+        if (r < rows_here) *reinterpret_cast<u32x4*>(p.out + (int64_t(r0 + r) * p.H + h) * kD + c * 8) = x;
+      }
+    } else {
+      const int qrow = r0 + l32;
+      if (qrow < it.q_end) {
+        const int64_t slot = (int64_t(it.split) * p.G + (qrow - p.frame_rows)) * p.H + h;
+        float* po = p.part_o + slot * kD;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g4 + 4 * hh) =
+                f32x4{oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
+                      oacc[qb][db][4 * g4 + 3]} * p.scale_v;
+        if (hh == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run[qb] * c2, l_tot);
+      }
+    }
+  };
+
+  // ---- Items of at most 64 rows (at H3 the last rows of every 2880-row group) run split
+  // over the four waves: wave w takes the 32-row block qs = w & 1 and the 32-key half
+  // kh = w >> 1 of every tile, through the same ring, loads and barriers.  In registers the
+  // half is key block 0 (its K and V rows are read 32 rows further for kh = 1); P words 4..7
+  // and the V fragments' second half stay zero, so each PV matrix op (64 keys) sees only
+  // this half.  Per tile:
+  //   slot A: S(t) = K(t) Q^T (2 ops)        | second half of the loads of t+2
+  //   barrier: tile t+1 has landed for every wave
+  //   slot B: O += V(t-1)^T P(t-1)^T, l += 1 P(t-1)^T (5 ops) | P(t) words 0..3, V(t) reads,
+  //           K(t+1) reads, first half of the loads of t+3; then the slow path of t if due
+  // P(t) is written while the PV ops read P(t-1): P alternates between pb[0] and pb[1] and
+  // the tile loop is unrolled twice.  The key halves merge by log-sum-exp through the LDS.
+  if (!causal && it.q_end - it.q_begin <= kWaveRows) {
+    const int qs = wave & 1, kh = wave >> 1;
+    const int r0q = it.q_begin + 32 * qs;
+    f32x16& sq = s0_split;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) koff[s][0] += uint32_t(kh * 32 * kD), koff[s][1] += uint32_t(kh * 32 * kD);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) voff[db] += uint32_t(kh * 32 * kD);
+    pb[0] = pb[1] = i32x8{};
+    {
+      const uint32_t toff0 = tile_off(0);
+#pragma unroll
+      for (int idx = 0; idx < kNLD; ++idx) dma_load(0, idx, toff0);
+    }
+    {
+      const int qrow = r0q + l32;
+      const bool ok = qrow < it.q_end;
+      const unsigned char* src = p.q + (int64_t(qrow) * p.H + h) * kD + 32 * hh;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (ok) {
+          a = *reinterpret_cast<const u32x4*>(src + 64 * s);
+          b = *reinterpret_cast<const u32x4*>(src + 64 * s + 16);
+        }
+        qf[0][s] = i32x8{int(a[0]), int(a[1]), int(a[2]), int(a[3]), int(b[0]), int(b[1]), int(b[2]), int(b[3])};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    uint32_t toff_q = tile_off(1);
+#pragma unroll
+    for (int idx = 0; idx < kNLD; ++idx) dma_load(1, idx, toff_q);
+    toff_q = tile_off(2);
+#pragma unroll
+    for (int idx = 0; idx < kNLD / 2; ++idx) dma_load(2, idx, toff_q);
+    barrier();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) read_k(4 * s), read_k(4 * s + 1);  // key block 0 of both k-steps
+#pragma unroll
+    for (int s = 0; s < 2; ++s) koff[s][0] += ring(1), koff[s][1] += ring(1);
+
+    // one step of slot B: FMAs and exponentials of word fe, packing (high half first, around
+    // the exponentials) and the max of word pk, into register set buf
+    auto step_q = [&](int buf, int pk, int fe) __attribute__((always_inline)) {
+      if (fe >= 0) {
+        float* f = fb[fe & 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = __builtin_fmaf(sq[4 * fe + j], c2, -mc[0]);
+        asm volatile("" ::"v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]));
+        if (fe == 0) pm[0] = 0.f;
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      int y = 0;
+      if (pk >= 0) {
+        const float* f = fb[pk & 1];
+        pm[0] = __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(pm[0], f[0]), f[1]), f[2]), f[3]);
+        asm volatile("" ::"v"(pm[0]));
+        y = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], pb[buf][pk], true);
+        asm volatile("" ::"v"(y));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (fe >= 0) {
+        float* f = fb[fe & 1];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) f[j] = __builtin_amdgcn_exp2f(f[j]);
+        asm volatile("" ::"v"(f[0]), "v"(f[1]), "v"(f[2]), "v"(f[3]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (pk >= 0) {
+        const float* f = fb[pk & 1];
+        pb[buf][pk] = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], y, false);
+        asm volatile("" ::"v"(pb[buf][pk]));
+      }
+    };
+    // slow path of tile t: mask keys past the segment end, raise the max of rows whose max
+    // grew by more than 2^8, words 0..3 of P(t) again
+    auto slow_q = [&](int buf, int t) __attribute__((always_inline)) {
+      int n0, nend;
+      tile_range(t, n0, nend);
+      const int valid = nend - n0;
+      if (valid < kBN) {
+        const int lim = valid - 32 * kh - 4 * hh;  // key (32 kh + (i/4)*8 + 4*hh + i%4) >= valid
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sq[i] = ((i >> 2) * 8 + (i & 3)) >= lim ? -__builtin_inff() : sq[i];
+      }
+      float mt = sq[0];
+#pragma unroll
+      for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, sq[i]);
+      const f32x2 o = other_half(mt);
+      mt = __builtin_fmaxf(o[0], o[1]);
+      const bool grow = mt > m_run[0] + lazy_raw;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float m_new = grow ? mt : m_run[0];
+        const float alpha = __builtin_amdgcn_exp2f((m_run[0] - m_new) * c2);
+        m_run[0] = m_new;
+        mc[0] = m_new * c2;
+        lacc[0] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) oacc[0][db] *= alpha;
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        float x[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sq[4 * w + j], c2, -mc[0]));
+        const int y = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pb[buf][w], true);
+        pb[buf][w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], y, false);
+      }
+    };
+    // slot B's matrix op i: four d-blocks of O, then the row sums
+    auto pv_q = [&](int buf, int i) __attribute__((always_inline)) {
+      if (i < 4) oacc[0][i] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[i], pb[buf], oacc[0][i], 0, 0, 0, 0, 0, 0);
+      else lacc[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(ones, pb[buf], lacc[0], 0, 0, 0, 0, 0, 0);
+    };
+    int nd = 0;  // next tile that takes the slow path
+    auto tile_q = [&](int t, auto cur_c) __attribute__((always_inline)) {
+      constexpr int cur = decltype(cur_c)::value;  // register set of P(t); P(t-1) is in the other
+      const uint32_t step_k = ring(t + 2) - ring(t + 1);
+      const uint32_t step_v = ring(t + 1) - ring(t);
+      const bool dirty = t == nd;
+      if (__builtin_expect(dirty, 0)) nd = next_dirty(t);
+      __builtin_amdgcn_s_waitcnt(kLgkmcnt0);
+      __builtin_amdgcn_sched_barrier(0);
+      // slot A
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        sq = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[s][0], qf[0][s], s == 0 ? zero : sq, 0, 0, 0, 0, 0, 0);
+        dma_load(t + 2, kNLD / 2 + s, toff_q);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kNLD);  // tile t+1 has landed (t+2 may be in flight) ...
+      barrier();                                   // ... for every wave
+      toff_q = next_off(t + 3, toff_q);
+      // slot B
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        pv_q(cur ^ 1, i);
+        __builtin_amdgcn_sched_barrier(0);
+        if (i < 4) {
+          read_v(i, 0);
+          read_v(i, 1);
+        }
+        if (i < 2) read_k(4 * i), read_k(4 * i + 1);
+        if (i == 0 || i == 2) dma_load(t + 3, i / 2, toff_q);
+        step_q(cur, i - 1, i < 4 ? i : -1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int db = 0; db < 4; ++db) voff[db] += step_v;
+#pragma unroll
+      for (int s = 0; s < 2; ++s) koff[s][0] += step_k, koff[s][1] += step_k;
+      asm volatile("" ::"v"(pb[cur][0]), "v"(pb[cur][1]), "v"(pb[cur][2]), "v"(pb[cur][3]), "v"(pm[0]));
+      if (dirty || __builtin_amdgcn_ballot_w64(pm[0] > kWeightLimit) != 0) slow_q(cur, t);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int t = 0; t < nt; t += 2) {
+      tile_q(t, std::integral_constant<int, 0>{});
+      if (t + 1 < nt) tile_q(t + 1, std::integral_constant<int, 1>{});
+    }
+    // PV of the last tile
+    if ((nt - 1) & 1) {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) pv_q(1, i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 5; ++i) pv_q(0, i);
+    }
+    // merge the key halves: the kh = 1 wave of each block leaves O (64 floats per lane, in
+    // lane order) and its (max, row sum) in the idle ring; the kh = 0 wave, whose lanes own
+    // the same rows and columns, merges them and writes the block
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);  // the ring's last loads have landed ...
+    barrier();                            // ... and no wave reads it any more
+    unsigned char* const mb = smem + qs * (16 * 1024 + 512);
+    if (kh == 1) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4)
+          *reinterpret_cast<f32x4*>(mb + (db * 4 + g4) * 1024 + lane * 16) =
+              f32x4{oacc[0][db][4 * g4], oacc[0][db][4 * g4 + 1], oacc[0][db][4 * g4 + 2], oacc[0][db][4 * g4 + 3]};
+      *reinterpret_cast<f32x2*>(mb + 16 * 1024 + lane * 8) = f32x2{m_run[0], lacc[0][0]};
+    }
+    barrier();
+    if (kh == 0) {
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(mb + 16 * 1024 + lane * 8);
+      const float m_new = __builtin_fmaxf(m_run[0], ml[0]);
+      const float a0 = __builtin_amdgcn_exp2f((m_run[0] - m_new) * c2), a1 = __builtin_amdgcn_exp2f((ml[0] - m_new) * c2);
+      m_run[0] = m_new;
+      lacc[0][0] = lacc[0][0] * a0 + ml[1] * a1;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(mb + (db * 4 + g4) * 1024 + lane * 16);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) oacc[0][db][4 * g4 + j] = oacc[0][db][4 * g4 + j] * a0 + x[j] * a1;
+        }
+      output_block(0, r0q);
+    }
+    return;
+  }
+
   // prologue: tile 0 and the Q fragments land together; then tile 1 and the first half of
   // tile 2 go in flight
   {
@@ -562,55 +825,8 @@ void attn_fp8_kernel(Fp8Params p) {
   check_block(1, s1, nt - 1, dirty_prev);
   pv_slot(1, [&](int) __attribute__((always_inline)) {});
 
-  // ---- Output.  A lane holds 4-column pieces of its row spread over the row; each 32-row
-  // block goes through this wave's LDS staging area (16-byte chunks XOR-swizzled by row) and
-  // leaves as whole rows, 16 lanes x 16 bytes per row.  Global-leg partials (fp32, already
-  // times scale_v) go straight out.
-  unsigned char* const stage = smem + kRingB + wave * kStageB;
-  // lane indices redefined here (empty asm) so that the staging addresses are computed here
-  // and not hoisted out of the unit loop into the tile loop's register budget
-  int orow_l = l32, olane = lane;
-  asm volatile("" : "+v"(orow_l), "+v"(olane));
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int rows_here = it.q_end - (row0 + 32 * qb);
-    if (rows_here <= 0) continue;
-    const float l_tot = lacc[qb][0];  // every element holds the row sum over both halves
-    if (it.split < 0) {
-      const float mul = p.scale_v / l_tot;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const int off = (32 * db + 8 * g4) * 2 + 8 * hh;  // byte offset in the row
-          unsigned char* dst = stage + orow_l * (kD * 2) + (((off >> 4) ^ (orow_l & 15)) << 4) + (off & 15);
-          *reinterpret_cast<u32x2*>(dst) =
-              u32x2{pack_bf16x2(oacc[qb][db][4 * g4] * mul, oacc[qb][db][4 * g4 + 1] * mul),
-                    pack_bf16x2(oacc[qb][db][4 * g4 + 2] * mul, oacc[qb][db][4 * g4 + 3] * mul)};
-        }
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = k * 64 + olane, r = j >> 4, c = j & 15;
-        const u32x4 x = *reinterpret_cast<const u32x4*>(stage + r * (kD * 2) + ((c ^ (r & 15)) << 4));
-        if (r < rows_here)
-          *reinterpret_cast<u32x4*>(p.out + (int64_t(row0 + 32 * qb + r) * p.H + h) * kD + c * 8) = x;
-      }
-    } else {
-      const int qrow = row0 + 32 * qb + l32;
-      if (qrow < it.q_end) {
-        const int64_t slot = (int64_t(it.split) * p.G + (qrow - p.frame_rows)) * p.H + h;
-        float* po = p.part_o + slot * kD;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4)
-            *reinterpret_cast<f32x4*>(po + 32 * db + 8 * g4 + 4 * hh) =
-                f32x4{oacc[qb][db][4 * g4], oacc[qb][db][4 * g4 + 1], oacc[qb][db][4 * g4 + 2],
-                      oacc[qb][db][4 * g4 + 3]} * p.scale_v;
-        if (hh == 0) *reinterpret_cast<float2*>(p.part_ml + slot * 2) = make_float2(m_run[qb] * c2, l_tot);
-      }
-    }
-  }
+  for (int qb = 0; qb < 2; ++qb) output_block(qb, row0 + 32 * qb);
   };  // run_item
 
   for (int n = 0;; ++n) {

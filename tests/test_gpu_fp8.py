@@ -141,6 +141,33 @@ def test_fp8_edge_geometries(gpu_lib, geom, H):
     _check(got, ref, np.nanmax(np.abs(decode_e4m3(v8))) * sv, f"edge {geom} H={H}")
 
 
+def test_fp8_short_items(gpu_lib):
+    """Items of at most 64 rows (three 300-row groups ending in 44-row items, a 30-row
+    global item) run split over the four waves by key half and merge the halves at the end.
+    Full comparison on random inputs; constant value rows exact (the merged row sum must be
+    the sum of exactly the rounded weights of both halves); q = k at a large scale exact
+    (each row's own key sits in one half, far above everything in the other)."""
+    T, S, G, K, r, H = 9, 100, 30, 3, 1, 2
+    geom = Geometry(T, S, G, K, r)
+    L = T * S + G
+    plan = gpu_lib.wa_plan_create(T, S, G, K, r, H, 128)
+    g = torch.Generator().manual_seed(12)
+    (q8, sq), (k8, sk), (v8, sv) = (quantize_e4m3(torch.randn(L, H, 128, generator=g)) for _ in range(3))
+    got = _run(gpu_lib, plan, q8, k8, v8, sq, sk, sv)
+    ref = fp8_window_attention_reference(q8, k8, v8, sq, sk, sv, geom)
+    _check(got, ref, np.nanmax(np.abs(decode_e4m3(v8))) * sv, "short items")
+    row, svc = quantize_e4m3(torch.randn(1, 1, 128, generator=g))
+    vc = row.expand(L, H, 128).contiguous()
+    got = _run(gpu_lib, plan, q8, k8, vc, sq, sk, svc)
+    _check_exact(got, np.broadcast_to(decode_e4m3(row) * svc, got.shape), "short items, constant values")
+    k8, sk = quantize_e4m3(torch.randn(L, H, 128, generator=g) * 2.5)
+    got = _run(gpu_lib, plan, k8, k8, v8, sk, sk, sv)
+    rows = [0, 255, 256, 299, 300, 599, 856, 899, T * S, L - 1]
+    ref = fp8_window_attention_rows(k8, k8, v8, sk, sk, sv, geom, rows, list(range(H)))
+    np.testing.assert_allclose(ref, decode_e4m3(v8[rows]) * sv, rtol=1e-6, atol=1e-6)  # the premise
+    _check_exact(got[rows], ref, "short items, self attention")
+
+
 def test_fp8_covers_every_row_and_is_deterministic(gpu_lib):
     """Every output element is written (NaN prefill), and two calls agree bit for bit."""
     w = WORKLOADS["ragged"]
