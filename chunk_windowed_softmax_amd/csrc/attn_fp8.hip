@@ -28,7 +28,10 @@
 // four weights (FMA, exp2, e4m3 packing, max) slightly longer (v_exp_f32 issues in about 10
 // cycles), so one group of four weights rides beside each matrix op and the kernel is bound
 // by vector issue, not by the matrix pipe.  A wave whose rows lie past the end of an item runs
-// a loop of its own that only takes its share of the tile loads and the barriers.
+// a loop of its own that only takes its share of the tile loads and the barriers.  An item
+// of at most 64 rows (at H3 the last rows of every group) is instead split over all four
+// waves: 32 rows and one 32-key half of every tile each, the halves merged by log-sum-exp
+// through the LDS.
 // Softmax: online over the tiles in the log2 domain, weights against a lazily raised running
 // max (they may reach 2^8, exact in e4m3, whose largest finite value is 448, before it
 // rises).  A block's tile takes the wave-uniform slow path when some weight exceeds 2^8, and
