@@ -20,10 +20,12 @@ Prints ONE JSON line.  ``--gpus N`` with N > 1 is refused: this build runs on on
 from __future__ import annotations
 
 import argparse
+import glob
 import json
 import os
 import statistics
 import sys
+import threading
 import time
 
 MFMA_BF16_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
@@ -117,17 +119,89 @@ def recorded_traffic(workload: str, kernel: str = "attn_kernel"):
     return rec["traffic_bytes"], rec
 
 
-def _time_calls(fn, steps: int, warmup: int, stream):
+class SclkSampler:
+    """The GPU's current shader clock while the timed calls run: the "S:" (current) line of
+    the card's pp_dpm_sclk in sysfs, which is the figure `rocm-smi --showclocks` prints, read
+    every 5 ms by a thread.  The card is the one at the PCI address of torch's device 0 (else
+    the only AMD card with that file).  `stats()` is None where the file is missing."""
+
+    def __init__(self):
+        self.path = self._find()
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = None
+
+    @staticmethod
+    def _find():
+        cards = []
+        for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+            try:
+                with open(os.path.join(dev, "vendor")) as f:
+                    if f.read().strip() == "0x1002" and os.path.exists(os.path.join(dev, "pp_dpm_sclk")):
+                        cards.append(dev)
+            except OSError:
+                pass
+        try:
+            import torch
+
+            pr = torch.cuda.get_device_properties(0)
+            addr = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}."
+            for dev in cards:
+                if os.path.basename(os.path.realpath(dev)).startswith(addr):
+                    return os.path.join(dev, "pp_dpm_sclk")
+        except (AttributeError, RuntimeError):
+            pass
+        return os.path.join(cards[0], "pp_dpm_sclk") if len(cards) == 1 else None
+
+    def _read(self):
+        with open(self.path) as f:
+            for line in f:
+                if line.rstrip().endswith("*"):
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            try:
+                mhz = self._read()
+            except (OSError, ValueError, IndexError):
+                return
+            if mhz is not None:
+                self.samples.append(mhz)
+            self._stop.wait(0.005)
+
+    def start(self):
+        if self.path is not None:
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+
+    def stop(self):
+        self._stop.set()
+        if self._thread is not None:
+            self._thread.join(timeout=1.0)
+
+    def stats(self):
+        if not self.samples:
+            return None
+        return {"median": statistics.median(self.samples), "min": min(self.samples), "max": max(self.samples),
+                "samples": len(self.samples),
+                "source": f"current shader clock, {self.path} (as rocm-smi --showclocks), every 5 ms over the "
+                          "timed calls"}
+
+
+def _time_calls(fn, steps: int, warmup: int, stream, sampler: SclkSampler | None = None):
     """Warm up, then time `steps` calls back to back: HIP events on the launch stream at the
     start and the end of the timed region (no event between calls, so the host enqueues ahead
     of the device) and the wall clock around it (synchronised on both sides).  Returns
-    (device ms per call, wall ms per call)."""
+    (device ms per call, wall ms per call).  A sampler, if given, runs over the timed region."""
     import torch
 
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if sampler is not None:
+        sampler.start()
     t0 = time.perf_counter()
     start.record(stream)
     for _ in range(steps):
@@ -135,7 +209,24 @@ def _time_calls(fn, steps: int, warmup: int, stream):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if sampler is not None:
+        sampler.stop()
     return start.elapsed_time(end) / steps, wall * 1e3 / steps
+
+
+def _time_each(fn, steps: int, stream):
+    """A second pass of `steps` calls with a HIP event on the launch stream between
+    consecutive calls: (median, min) device ms per call."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    ts = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return statistics.median(ts), min(ts)
 
 
 def _calibration_copy(x):
@@ -173,8 +264,10 @@ def bench_fp8(args, w) -> int:
     stream = torch.cuda.current_stream(dev)
     if args.calibration_copy:
         _calibration_copy(q8)
-    dev_ms, ms_step = _time_calls(lambda: wa.wa_forward_fp8(plan, q8, k8, v8, sq, sk, sv, out=out, stream=stream),
-                                  args.steps, args.warmup, stream)
+    call = lambda: wa.wa_forward_fp8(plan, q8, k8, v8, sq, sk, sv, out=out, stream=stream)  # noqa: E731
+    sclk = SclkSampler()
+    dev_ms, ms_step = _time_calls(call, args.steps, args.warmup, stream, sclk)
+    med_ms, min_ms = _time_each(call, args.steps, stream)
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (dev_ms * 1e-3) / 1e12
     traffic, traffic_rec = recorded_traffic(w.name, "attn_fp8_kernel")
@@ -197,7 +290,10 @@ def bench_fp8(args, w) -> int:
             "H": w.H, "d": w.d, "L": w.L, "kept_pairs": info["kept_pairs_per_head"] * w.H,
             "flop_per_call": flop, "scales": "per tensor", "parallelism": "single GPU",
         },
-        "ms_per_call": {"device_mean": round(dev_ms, 4)},
+        "ms_per_call": {"device_mean": round(dev_ms, 4), "median": round(med_ms, 4), "min": round(min_ms, 4),
+                        "median_min_from": "a second pass of as many calls, HIP events between consecutive calls"},
+        "tflops_at_median": round(flop / (med_ms * 1e-3) / 1e12, 2),
+        "sclk_mhz": sclk.stats(),
         "plan_create_ms": round(plan_ms, 3),
         "roofline": {
             "bound": "mfma",
@@ -425,7 +521,10 @@ def main() -> int:
         # one read + one write of q.numel()*2 bytes per copy; profiled beside the attention
         _calibration_copy(q)
 
-    dev_ms, ms_step = _time_calls(wa.prepared_forward(plan, q, k, v, out, stream), args.steps, args.warmup, stream)
+    call = wa.prepared_forward(plan, q, k, v, out, stream)
+    sclk = SclkSampler()
+    dev_ms, ms_step = _time_calls(call, args.steps, args.warmup, stream, sclk)
+    med_ms, min_ms = _time_each(call, args.steps, stream)
 
     value = flop / (ms_step * 1e-3) / 1e12
     achieved = flop / (dev_ms * 1e-3) / 1e12
@@ -454,8 +553,11 @@ def main() -> int:
             "flop_per_call": flop, "n_groups": info["n_groups"], "n_splits": info["n_splits"],
             "parallelism": "single GPU",
         },
-        "ms_per_call": {"device_mean": round(dev_ms, 4)},
+        "ms_per_call": {"device_mean": round(dev_ms, 4), "median": round(med_ms, 4), "min": round(min_ms, 4),
+                        "median_min_from": "a second pass of as many calls, HIP events between consecutive calls"},
+        "tflops_at_median": round(flop / (med_ms * 1e-3) / 1e12, 2),
         "pct_of_bf16_peak": round(100 * value / MFMA_BF16_PEAK_TFLOPS, 2),
+        "sclk_mhz": sclk.stats(),
         "plan_create_ms": round(plan_ms, 3),
         "roofline": {
             "bound": "mfma",
