@@ -853,7 +853,8 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
         const int tt = i / DB, db = i % DB;
         oacc[0][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vfrag(0, tt, db), pfrag(buf, 0, tt), oacc[0][db], 0, 0, 0);
       };
-      // tile t-1's verdict, with its pairs complete (register set `buf`)
+      // tile t's verdict once all its pairs are done (register set `buf`); then its row sums
+      // join the running sum
       auto check_q = [&](int buf, int t, bool dirty) __attribute__((always_inline)) {
         asm volatile("" ::"v"(pw[buf][0]), "v"(pw[buf][1]), "v"(pw[buf][2]), "v"(pw[buf][3]), "v"(pw[buf][4]),
                      "v"(pw[buf][5]), "v"(pw[buf][6]), "v"(pw[buf][7]), "v"(rs[buf][0]), "v"(rs[buf][1]));
