@@ -99,6 +99,7 @@ def test_h3_full_sampled_parity(gpu_lib):
     ((40, 48, 200, 1, 2), 2, 64, torch.bfloat16),  # K = 1, many groups, split global leg
     ((6, 300, 40, 1, 1), 2, 128, torch.bfloat16),  # 44-row window and 40-row global items
     ((7, 60, 33, 1, 2), 3, 64, torch.float32),     # every item one wave (60-row chunks)
+    ((9, 100, 30, 3, 1), 2, 128, torch.float32),   # fp32 out of the split 44-row and 30-row items
 ])
 def test_edge_geometries(gpu_lib, geom, H, d, dtype):
     T, S, G, K, r = geom
