@@ -13,7 +13,7 @@ Source (web page; cited by title and section):
   cast to that backend's dtype for the attention only, the output being returned in the
   input dtype.
 
-Readings taken where the page is silent (each also listed in the design doc):
+Readings taken where the page is silent:
 
 * Causal means query row i sees key rows 0..i (queries and keys have the same length,
   so the usual top-left alignment); the scale is SDPA's default 1/sqrt(head_dim).

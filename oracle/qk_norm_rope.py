@@ -15,7 +15,7 @@ Sources (web pages; cited by title and section):
   out-of-place kernel normalises q and k, applies RoPE and writes them (and v) to their
   destination, instead of an in-place norm followed by a copy.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 
 * The norm is RMSNorm over each (token, head) vector of head_dim channels:
   ``y = x / sqrt(mean(x^2) + eps) * w``, with an optional per-channel weight ``w`` shared

@@ -19,7 +19,7 @@ Sources (web pages; cited by title and section):
   backend" -- the ``[B, L, H, d]`` q/k/v layout (``qkv.view(B, L, H, 3*d)``), the
   non-causal dense decoder, and SDPA called with its default 1/sqrt(d) scale.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 
 * Row order: frames first, frame-major (row = t*S + s), then the G global rows.
 * Windows are clipped to chunks [0, C-1]; the last chunk may hold fewer than K frames.
