@@ -42,11 +42,12 @@
 //   per-lane clamping at segment or tensor ends.  LDS rows hold d bf16; 16-byte chunks are
 //   XOR-swizzled per row (applied on the global side of the DMA) so the K reads and the
 //   transpose reads are free of bank conflicts.
-//   The running max is raised lazily: exponentials are taken against the running max,
-//   and a wave-uniform slow path raises the max of each row whose max grew by more than
-//   2^8 (rescaling its accumulators; values up to 2^8 are exact in the softmax ratio);
-//   the same path masks keys past a segment end.  Whether a tile needs it for reasons other
-//   than its data (first tile, masked keys) is known before the tile: one scalar compare.
+//   The running max is raised lazily: exponentials are taken against the running max as it
+//   stands, and only when some weight of a tile may exceed 2^8 (its row sums exceed 2^8)
+//   does a wave-uniform slow path find the tile max and raise each row's max to it
+//   (rescaling its accumulators); the same path masks keys past a segment end.  Whether a
+//   tile needs it for reasons other than its data (first tile, masked keys) is known before
+//   the tile: one scalar compare.
 //   The launch is persistent: one block per CU takes work units from its XCD's queue in the
 //   plan's launch order (blocks are dispatched round-robin over the XCDs), a contiguous run
 //   of window units, so the query tiles of one group run side by side and share that XCD's
@@ -159,7 +160,6 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   constexpr int KS = D / 16;                    // MFMA k-steps over d
   constexpr int DB = D / 32;                    // 32-wide output column blocks
   static_assert(NJ % kNW == 0, "tile slices must divide evenly over the waves");
-  constexpr float kLazyLog2 = 8.f;              // slow path: rescale only when the max grows by > 2^8
   constexpr float kRowSumLimit = 256.f;         // fast path only while every P of the tile <= 2^8
   // d = 64: the row sums of P come from matrix ops against an all-ones operand (four per
   // block and tile, at the end of the PV slot) instead of vector adds.  At d = 64 a tile has
@@ -314,9 +314,9 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   constexpr int NLD = 2 * JPW;  // DMA loads per tile per wave
 
   const float c2 = p.scale_log2;
-  const float lazy_raw = kLazyLog2 / c2;
-  // Initial running max: finite (every weight against it is zero, and every finite score
-  // exceeds it by more than 2^8, so the first tile, which takes the slow path, raises it).
+  // Initial running max: finite (so a rescale factor is never exp2 of inf - inf) and below
+  // every finite score; the first tile of a unit always takes the slow path, which raises it
+  // before any weight is used.
   constexpr float kMaxInit = -0x1p100f;
 
   float m_run[2], mc[2], l_run[2];  // running max of raw scores (this lane's queries), * c2, sum
@@ -431,7 +431,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
   // vector ops back to back.
   // Slow path.  The exponentials are taken against the running max as it stands; a block's
   // tile goes to the slow path (wave-uniform), which finds the tile max and raises the
-  // running max when it grew by more than 2^8, when
+  // running max of every row whose tile max exceeds it, when
   //   - it is the unit's first tile or has masked keys (segment end, causal diagonal): known
   //     before the tile, one scalar compare per tile;
   //   - some row sum of the tile exceeds 2^8 (any P above 2^8 makes it so; ONES: some P
@@ -492,10 +492,13 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) mt = __builtin_fmaxf(mt, sa[b][i]);
     mt = pair_max(mt);
-    // Only rows whose own max grew by more than 2^8 raise it (the branch is wave-uniform,
-    // the choice per row): the other rows keep their max and rescale by exactly 1, so a
-    // row's arithmetic never depends on the scores of the other rows in the wave.
-    const bool grow = mt > m_run[qb] + lazy_raw;
+    // Every row whose tile max exceeds its running max raises it to that max (the branch is
+    // wave-uniform, the choice per row): the other rows keep their max and rescale by
+    // exactly 1, so a row's arithmetic never depends on the scores of the other rows in the
+    // wave.  Raising to the exact max, not only past a 2^8 growth, matters for the row-sum
+    // test: a row whose weights sit between 2^3 and 2^8 on many keys trips it, and left at
+    // its old max it would trip it again on every following tile.
+    const bool grow = mt > m_run[qb];
     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
       const float m_new = grow ? mt : m_run[qb];
       const float alpha = fast_exp2((m_run[qb] - m_new) * c2);
@@ -813,8 +816,8 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
           }
         }
       };
-      // slow path of tile t: mask keys past the segment end, raise the max of rows whose max
-      // grew by more than 2^8, recompute P(t) into `buf`
+      // slow path of tile t: mask keys past the segment end, raise the max of every row whose
+      // tile max exceeds it, recompute P(t) into `buf`
       auto slow_q = [&](int buf, int t) __attribute__((always_inline)) {
         int k0, kend;
         tile_range(t, k0, kend);
@@ -828,7 +831,7 @@ void attn_kernel(std::conditional_t<TL, AttnParamsTL, AttnParams> p) {
 #pragma unroll
         for (int i = 1; i < 16; ++i) mt = __builtin_fmaxf(mt, sq[buf][i]);
         mt = pair_max(mt);
-        const bool grow = mt > m_run[0] + lazy_raw;
+        const bool grow = mt > m_run[0];
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
           const float m_new = grow ? mt : m_run[0];
           const float alpha = fast_exp2((m_run[0] - m_new) * c2);
